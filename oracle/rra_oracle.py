@@ -1,0 +1,308 @@
+"""Plain, slow CPU oracle for RRAttention block-sparse prefill attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke entry point and the
+CPU-baseline leg of the benchmark may import this module. The library's
+product path never calls it, and this module imports nothing from the HIP path.
+
+Everything is computed in float64 with numpy, head by head, in the order the
+method is described in
+
+    "RRAttention: Dynamic Block Sparse Attention via Per-Head Round-Robin
+    Shifts for Long-Context Inference" (arXiv 2602.05853):
+      §2.1 Block-wise Sparse Attention        -- block partition, stride S
+      §3.1 Query Sampling with Head Round-Robin Strategy
+      §3.2 Stride-level Importance Estimation -- stride scores, 1/(S*sqrt(d))
+      §3.3 Block-level Selection via Top-tau Thresholding
+      §4.1 Settings                           -- prefill only, FlashAttention baseline
+      §4.3 Ablation Study                     -- last-query-block protection
+      §7   Limitations                        -- S > H coverage gap
+    and the XAttention summary page (arXiv 2503.16428), "Key points": keep the
+    minimal set of blocks whose cumulative normalised score reaches tau.
+
+Several displayed equations of the RRAttention page were lost (the sampling
+formula of §3.1, the score equation of §3.2, all of §3.3).  The readings used
+here are:
+
+  * sampled position  P(i, h) = i*S + (h mod S)                    (§3.1, §7)
+  * aggregated key    Kagg[j] = bf16_rne( (sum of K over stride j) / S )
+                      -- the 1/S of the §3.2 normalisation folded into the
+                      stride mean; the bf16 rounding is part of the library's
+                      contract ("none" skips it)
+  * stride score      s[i, j] = sm_scale * <Q[P(i,h)], Kagg[j]>,  j <= i
+  * stride softmax    per sampled query, over its visible strides (§2.2 query
+                      independence)
+  * block score       M[I, J] = (1/r) * sum_{i in I} sum_{j in J, j <= i} p[i, j],
+                      r = Bk / S, so every row of M sums to 1
+  * Top-tau           order J by (M desc, J asc); keep the first k* with
+                      cumulative mass >= tau * (row total); tau >= 1 or the
+                      protected last query-block row keeps all causal blocks
+  * attention         exact causal softmax attention restricted, per query,
+                      to keys in its selected key blocks
+
+Indices are 0-based.  GQA: query head h reads KV head h // (H / Hkv).
+
+Parity status: every function below is pinned by a CPU test against a closed
+form, a library routine, brute force or a hand-worked table.  Faithfulness of
+the readings above to the authors' own (unpublished) implementation is parity
+unpinned: the pages print no worked example.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "Params",
+    "bf16_round",
+    "rr_positions",
+    "aggregate_keys",
+    "stride_scores",
+    "stride_softmax",
+    "pool_blocks",
+    "block_scores",
+    "top_tau_row",
+    "select_blocks",
+    "estimate",
+    "block_sparse_attention",
+    "dense_attention",
+    "attention_rows",
+]
+
+
+@dataclass(frozen=True)
+class Params:
+    """Problem sizes and sparsity settings (RRAttention §2.1, §4.1)."""
+
+    batch: int
+    num_heads: int
+    num_kv_heads: int
+    seq_len: int
+    head_dim: int
+    stride: int  # S
+    block: int  # Bk (the page calls it B)
+    tau: float
+    protect_last: bool = True
+    sm_scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
+
+    @property
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group(self) -> int:
+        return self.num_heads // self.num_kv_heads
+
+    @property
+    def num_strides(self) -> int:
+        return self.seq_len // self.stride
+
+    @property
+    def num_blocks(self) -> int:
+        return self.seq_len // self.block
+
+    @property
+    def strides_per_block(self) -> int:
+        return self.block // self.stride
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (round to nearest, ties to even), from the definition.
+# ---------------------------------------------------------------------------
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (7 stored) and float32's exponent
+    range.  For |x| in [2^e, 2^(e+1)) the spacing of bf16 values is
+    2^(e-7); below 2^-126 (bf16 subnormals) the spacing is fixed at 2^-133.
+    Dividing by a power of two is exact in float64, and numpy's rint rounds
+    half to even, so x / ulp -> rint -> * ulp is the exact RNE result.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    nz = (x != 0) & np.isfinite(x)
+    _, ex = np.frexp(x[nz])  # x = m * 2^ex, 0.5 <= |m| < 1  ->  e = ex - 1
+    e = np.maximum(ex - 1, -126)
+    ulp = np.ldexp(1.0, e - 7)
+    r = np.rint(x[nz] / ulp) * ulp
+    if np.any(np.abs(r) >= 2.0**128):
+        raise OverflowError("value outside the bfloat16 finite range")
+    out[nz] = r
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# §3.1: head round-robin query sampling.
+# ---------------------------------------------------------------------------
+def rr_positions(num_strides: int, stride: int, head: int) -> np.ndarray:
+    """Token position sampled from each stride i for query head `head`.
+
+    One query per stride of S tokens; the offset inside the stride rotates
+    with the head index (RRAttention §1, §3.1 and the abstract) and does not
+    depend on i, so with S > H some offsets are never sampled (§7).
+    """
+    return np.arange(num_strides, dtype=np.int64) * stride + (head % stride)
+
+
+# ---------------------------------------------------------------------------
+# §3.2: stride-level key aggregation and scores.
+# ---------------------------------------------------------------------------
+def aggregate_keys(k_head: np.ndarray, stride: int, kagg_round: str = "bf16") -> np.ndarray:
+    """Mean of the S key vectors of every stride j, for one KV head.
+
+    k_head: [L, d] float64 holding bf16 values.  The sum of S <= 32 bf16
+    values is exact in float64 (it needs far fewer than 53 bits for any data
+    whose magnitudes span under 2^40), and /S is exact for a power-of-two S.
+    """
+    L, d = k_head.shape
+    sums = k_head.reshape(L // stride, stride, d).sum(axis=1)
+    mean = sums / stride
+    if kagg_round == "bf16":
+        return bf16_round(mean)
+    if kagg_round == "none":
+        return mean
+    raise ValueError(f"unknown kagg_round {kagg_round!r}")
+
+
+def stride_scores(q_head: np.ndarray, kagg: np.ndarray, stride: int, head: int,
+                  sm_scale: float) -> np.ndarray:
+    """s[i, j] = sm_scale * <Q[P(i, h)], Kagg[j]> for j <= i, -inf above.
+
+    With Kagg the stride mean, sm_scale = 1/sqrt(d) gives the page's
+    normalisation 1/(S*sqrt(d)) of Q_P(i,h) . sum_{t in stride j} K_t.
+    Every stride j <= i is visible, the diagonal stride included.
+    """
+    ns = kagg.shape[0]
+    qs = q_head[rr_positions(ns, stride, head)]  # [Ns, d]
+    s = sm_scale * (qs @ kagg.T)
+    s[np.triu_indices(ns, k=1)] = -np.inf
+    return s
+
+
+def stride_softmax(s: np.ndarray) -> np.ndarray:
+    """Softmax of every sampled query's row over its visible strides (§2.2)."""
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=1, keepdims=True)
+
+
+def pool_blocks(p: np.ndarray, strides_per_block: int) -> np.ndarray:
+    """M[I, J] = (1/r) * sum of p over the r x r stride cells of block (I, J)."""
+    ns = p.shape[0]
+    r = strides_per_block
+    nb = ns // r
+    return p.reshape(nb, r, nb, r).sum(axis=(1, 3)) / r
+
+
+def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "bf16") -> np.ndarray:
+    """Block-score matrices M for every (batch, query head): [Bz, H, Nb, Nb]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    nb = prm.num_blocks
+    out = np.zeros((prm.batch, prm.num_heads, nb, nb))
+    for b in range(prm.batch):
+        for g in range(prm.num_kv_heads):
+            kagg = aggregate_keys(k[b, g], prm.stride, kagg_round)
+            for hh in range(prm.group):
+                h = g * prm.group + hh
+                s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale)
+                out[b, h] = pool_blocks(stride_softmax(s), prm.strides_per_block)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# §3.3: Top-tau selection with last-query-block protection (§4.3).
+# ---------------------------------------------------------------------------
+def top_tau_row(m_row: np.ndarray, row: int, tau: float, protect: bool) -> np.ndarray:
+    """Selected key blocks (ascending) of query-block row `row`.
+
+    Candidates are J = 0..row (causal).  Keep all of them if tau >= 1 or the
+    row is protected; otherwise sort by (mass desc, J asc) and keep the
+    shortest prefix whose cumulative mass reaches tau times the row total.
+    """
+    n = row + 1
+    if tau >= 1.0 or protect:
+        return np.arange(n, dtype=np.int64)
+    vals = np.asarray(m_row[:n], dtype=np.float64)
+    order = np.lexsort((np.arange(n), -vals))  # last key is primary: mass desc, then J asc
+    csum = np.cumsum(vals[order])
+    total = np.sum(vals)
+    hit = np.nonzero(csum >= tau * total)[0]
+    k_star = int(hit[0]) + 1 if hit.size else n
+    return np.sort(order[:k_star])
+
+
+def select_blocks(m: np.ndarray, prm: Params):
+    """Block mask [Bz,H,Nb,Nb] u8, index lists [Bz,H,Nb,Nb] i32 and counts [Bz,H,Nb] i32."""
+    nb = prm.num_blocks
+    mask = np.zeros((prm.batch, prm.num_heads, nb, nb), dtype=np.uint8)
+    idx = np.full((prm.batch, prm.num_heads, nb, nb), -1, dtype=np.int32)
+    cnt = np.zeros((prm.batch, prm.num_heads, nb), dtype=np.int32)
+    for b in range(prm.batch):
+        for h in range(prm.num_heads):
+            for i in range(nb):
+                sel = top_tau_row(m[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1)
+                mask[b, h, i, sel] = 1
+                idx[b, h, i, : sel.size] = sel
+                cnt[b, h, i] = sel.size
+    return mask, idx, cnt
+
+
+def estimate(q, k, prm: Params, kagg_round: str = "bf16"):
+    """Whole estimator: returns (mask, idx, cnt, M)."""
+    m = block_scores(q, k, prm, kagg_round)
+    mask, idx, cnt = select_blocks(m, prm)
+    return mask, idx, cnt, m
+
+
+# ---------------------------------------------------------------------------
+# §4.1: block-sparse causal prefill attention and its dense baseline.
+# ---------------------------------------------------------------------------
+def _attend(qb: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_pos: np.ndarray,
+            q_pos: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Exact softmax attention of queries qb over the given keys, causally masked."""
+    s = sm_scale * (qb @ keys.T)
+    s[key_pos[None, :] > q_pos[:, None]] = -np.inf
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return (e @ vals) / np.sum(e, axis=1, keepdims=True)
+
+
+def attention_rows(q, k, v, mask, prm: Params, b: int, h: int, row: int) -> np.ndarray:
+    """Output rows of query block `row` of head h, restricted to mask[b, h, row].
+
+    Query t attends to keys u <= t lying in a selected key block.  Returns
+    [Bk, d] float64.
+    """
+    bk = prm.block
+    g = h // prm.group
+    sel = np.nonzero(np.asarray(mask[b, h, row][: row + 1]))[0]
+    if sel.size == 0:
+        raise ValueError("empty selection")
+    key_pos = (sel[:, None] * bk + np.arange(bk)[None, :]).reshape(-1)
+    q_pos = row * bk + np.arange(bk)
+    qb = np.asarray(q[b, h, q_pos], dtype=np.float64)
+    keys = np.asarray(k[b, g, key_pos], dtype=np.float64)
+    vals = np.asarray(v[b, g, key_pos], dtype=np.float64)
+    return _attend(qb, keys, vals, key_pos, q_pos, prm.scale)
+
+
+def block_sparse_attention(q, k, v, mask, prm: Params) -> np.ndarray:
+    """O[b, h] for every query block, over the selected key blocks only."""
+    out = np.zeros((prm.batch, prm.num_heads, prm.seq_len, prm.head_dim))
+    bk = prm.block
+    for b in range(prm.batch):
+        for h in range(prm.num_heads):
+            for i in range(prm.num_blocks):
+                out[b, h, i * bk:(i + 1) * bk] = attention_rows(q, k, v, mask, prm, b, h, i)
+    return out
+
+
+def dense_attention(q, k, v, prm: Params) -> np.ndarray:
+    """Dense causal attention: every causal key block selected."""
+    nb = prm.num_blocks
+    full = np.broadcast_to(np.tril(np.ones((nb, nb), dtype=np.uint8)),
+                           (prm.batch, prm.num_heads, nb, nb))
+    return block_sparse_attention(q, k, v, full, prm)
