@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of RRAttention block-sparse causal prefill on one MI355X.
+
+One step = the whole hot path on one attention layer of the headline
+workload (Llama-3-8B shape: 32 query heads, 8 KV heads, d = 128, L = 131072,
+S = 16, Bk = 128, tau = 0.9): rra_estimate (stride aggregation, round-robin
+sampled scores + stride softmax + block pooling, Top-tau selection) followed
+by rra_sparse_attn.  Inputs are seeded synthetic bf16 tensors already resident
+in HBM when the timed region starts.  The dense causal flash attention of the
+same library is timed on the same inputs for the speedup.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload llama_128k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=1, n_rows_sample=4):
+    """The fp64 CPU oracle on a bounded sample of the same workload.
+
+    Times the oracle's estimator on n_heads_sample query heads (full length)
+    and its attention on n_rows_sample sampled (head, query block) rows (on the
+    GPU's mask), then extrapolates to the whole layer: the estimator by head
+    count, the attention by the number of selected key blocks."""
+    import numpy as np
+    import torch
+    from oracle import rra_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([d.get("num_threads", 1) for d in info] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    prm = orc.Params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block,
+                     float(np.float32(w.tau)), True)
+    nb = prm.num_blocks
+    t0 = time.perf_counter()
+    for h in range(n_heads_sample):
+        g = h // prm.group
+        kagg = orc.aggregate_keys(k[0, g].double().numpy(), prm.stride)
+        s = orc.stride_scores(q[0, h].double().numpy(), kagg, prm.stride, h, prm.scale)
+        m = orc.pool_blocks(orc.stride_softmax(s), prm.strides_per_block)
+        for i in range(nb):
+            orc.top_tau_row(m[i], i, prm.tau, i == nb - 1)
+    t_est = (time.perf_counter() - t0) / n_heads_sample * w.num_heads * w.batch
+    rng = np.random.default_rng(0)
+    rows = [(0, int(rng.integers(0, w.num_heads)), int(rng.integers(nb // 2, nb))) for _ in range(n_rows_sample)]
+    qn = {}
+    t_attn_sample = 0.0
+    blocks_sample = 0
+    for (b, h, i) in rows:
+        g = h // prm.group
+        sub_q = q[b:b + 1, h:h + 1].double().numpy()
+        sub_k = k[b:b + 1, g:g + 1].double().numpy()
+        sub_v = v[b:b + 1, g:g + 1].double().numpy()
+        one = orc.Params(1, 1, 1, prm.seq_len, prm.head_dim, prm.stride, prm.block, prm.tau, True)
+        mrow = sel_mask[b:b + 1, h:h + 1]
+        t1 = time.perf_counter()
+        orc.attention_rows(sub_q, sub_k, sub_v, mrow, one, 0, 0, i)
+        t_attn_sample += time.perf_counter() - t1
+        blocks_sample += int(cnt[b, h, i])
+        qn[(b, h, i)] = True
+    t_attn = t_attn_sample / max(blocks_sample, 1) * float(cnt.sum())
+    t_total = t_est + t_attn
+    return {
+        "value": f_dense / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: estimator on {n_heads_sample} of {w.num_heads} heads at full length "
+                   f"({time.perf_counter() - t0:.1f} s wall incl. attention), attention on {n_rows_sample} sampled "
+                   f"(head, query-block) rows ({blocks_sample} key blocks); extrapolated to the whole layer "
+                   f"by heads and by selected blocks: {t_total:.0f} s per step"),
+        "extrapolated_s_per_step": t_total,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama_128k")
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "profiles", "traffic_sparse_attn_llama_128k.json"))
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by KV group "
+              "with no exchange, so run one process per GPU instead.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dynamic_block_sparse_sample_amd as rra
+    from dynamic_block_sparse_sample_amd import workloads as wl
+
+    rra.lib()  # fail loudly without the HIP library
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = wl.WORKLOADS[args.workload]
+    if w.fp32_inputs:
+        log("pick a bf16 workload for the benchmark")
+        return 2
+    log(f"[bench] generating {w.name} inputs (seed {w.seed})")
+    t0 = time.time()
+    q, k, v = wl.make_inputs(w)
+    log(f"[bench] generated in {time.time() - t0:.1f}s; copying to the GPU")
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block, w.tau)
+    nb = p.num_blocks
+    ws = rra.alloc_workspace(p, dev)
+    sel = rra.Selection(*rra._lib._selection_buffers(p, dev), None)
+    out = torch.empty_like(qd)
+    dense_out = torch.empty_like(qd)
+    torch.cuda.synchronize()
+
+    def step():
+        rra.estimate(p, qd, kd, workspace=ws, out=sel)
+        rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, end = E(), E()
+    sp_ev = [(E(), E()) for _ in range(args.steps)]
+    est_ev = [(E(), E()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        est_ev[i][0].record()
+        rra.estimate(p, qd, kd, workspace=ws, out=sel)
+        est_ev[i][1].record()
+        sp_ev[i][0].record()
+        rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)
+        sp_ev[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    t_sp = sum(a.elapsed_time(b) for a, b in sp_ev) / args.steps
+    t_est = sum(a.elapsed_time(b) for a, b in est_ev) / args.steps
+
+    # per-kernel breakdown of the estimator (same buffers)
+    kagg = ws[: p.batch * p.num_kv_heads * p.num_strides * p.head_dim * 2].view(torch.bfloat16).view(
+        p.batch, p.num_kv_heads, p.num_strides, p.head_dim)
+    score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=dev)
+    reps = 5
+    brk = {}
+    for name, fn in [("stride_aggregate", lambda: rra.stride_aggregate(p, kd, kagg)),
+                     ("block_scores", lambda: rra.block_scores(p, qd, kagg, score)),
+                     ("top_tau", lambda: rra.top_tau(p, score, sel.mask, sel.idx, sel.cnt))]:
+        fn()
+        a, b = E(), E()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        brk[name] = a.elapsed_time(b) / reps
+
+    log(f"[bench] dense baseline x{args.dense_reps}")
+    rra.dense_attn(p, qd, kd, vd, out=dense_out)
+    torch.cuda.synchronize()
+    a, b = E(), E()
+    a.record()
+    for _ in range(args.dense_reps):
+        rra.dense_attn(p, qd, kd, vd, out=dense_out)
+    b.record()
+    torch.cuda.synchronize()
+    t_dense = a.elapsed_time(b) / args.dense_reps
+
+    # the timed steps left the selection of this input in sel
+    cnt = sel.cnt.cpu()
+    sum_cnt = int(cnt.sum())
+    causal_blocks = p.batch * p.num_heads * nb * (nb + 1) // 2
+    density = sum_cnt / causal_blocks
+    L, d, Bk = w.seq_len, w.head_dim, w.block
+    f_dense = 4.0 * d * w.batch * w.num_heads * L * (L + 1) / 2
+    f_sel = 4.0 * d * Bk * Bk * sum_cnt
+    achieved = f_sel / (t_sp * 1e-3) / 1e12
+    value = f_dense / (ms_step * 1e-3) / 1e12
+    # algorithmic bytes of the estimator and of the aggregation kernel
+    ns = p.num_strides
+    k_bytes = w.batch * w.num_kv_heads * L * d * 2
+    kagg_b = w.batch * w.num_kv_heads * ns * d * 2
+    est_bytes = (k_bytes + w.batch * w.num_heads * ns * d * 2 + w.batch * w.num_heads * nb * nb
+                 + 4 * sum_cnt + 4 * w.batch * w.num_heads * nb)
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("kernel_source_hash") == _kernel_hash():
+                traffic = tj.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+    line = {
+        "metric": "sparse prefill attn latency + effective TFLOP/s at 128K; speedup vs dense; mask density",
+        "value": round(value, 2),
+        "unit": "TFLOP/s (dense-equivalent causal attention FLOPs / step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "seq_len": L, "head_dim": d, "stride": w.stride, "block": Bk, "tau": w.tau,
+                   "protect_last": True, "parallelism": "none (1 GPU)"},
+        "latency_ms": round(ms_step, 4),
+        "t_estimate_ms": round(t_est, 4),
+        "t_sparse_attn_ms": round(t_sp, 4),
+        "t_dense_attn_ms": round(t_dense, 4),
+        "speedup_vs_dense": round(t_dense / ms_step, 4),
+        "mask_density": round(density, 5),
+        "estimator_kernels_ms": {kk: round(vv, 4) for kk, vv in brk.items()},
+        "estimator_hbm_frac": round(est_bytes / (t_est * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (brk["stride_aggregate"] * 1e-3) / 1e9
+                                           / PEAK_HBM_GBS, 4),
+        "dense_attn_tflops": round(f_dense / (t_dense * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "flash_attn_kernel<128,128> (rra_sparse_attn)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": f_sel, "avg_launch_ms": round(t_sp, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline (bounded sample)")
+        cb = cpu_baseline(q, k, v, sel.mask.cpu().numpy(), cnt.numpy(), w, f_dense)
+        line["cpu_baseline"] = {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in cb.items()}
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _kernel_hash() -> str:
+    """Hash of the attention kernel source; traffic counters are only valid for it."""
+    import hashlib
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd", "csrc",
+                       "kernels", "flash_attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

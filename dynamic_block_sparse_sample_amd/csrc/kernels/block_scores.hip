@@ -1,0 +1,230 @@
+// Round-robin sampled stride scores, stride softmax and block pooling
+// (RRAttention §3.1 query sampling with head round-robin, §3.2 stride-level
+// importance estimation, §2.2 query independence).
+//
+// One wave per (batch, KV group g, query block I, row tile).  A row tile holds
+// 32 sampled queries: strides i of block I for the G query heads of group g,
+// taken at positions P(i,h) = i*S + (h mod S).  The wave computes the
+// transposed score tile S^T = Kagg_tile x Q_sampled^T with
+// v_mfma_f32_32x32x16_bf16 (A = 32 aggregated keys, B = 32 sampled queries),
+// so every lane owns one sampled query (lane & 31) and 16 of the 32 strides of
+// a tile; the other 16 live in lane ^ 32.  Row statistics (max, sum) are then
+// per-lane, with one cross-half exchange at the end.
+//
+// Two passes over the visible strides j <= i: pass 1 finds the row max and
+// the softmax denominator (online, base-2), pass 2 recomputes the scores,
+// normalises them and sums them into block cells
+//   score[b,h,I,J] = (1/r) sum_{i in I} sum_{j in J, j <= i} p[i,j]
+// with in-lane adds plus cross-lane xor shuffles over the r queries of a head.
+// Kagg tiles are read straight from L2 (16 bytes per lane per chunk, prefetched
+// one tile ahead); the aggregated keys of one KV head are 1/S of K and stay
+// cache-resident.
+#include <cmath>
+
+#include "../rra_internal.h"
+#include "rra_device.h"
+
+namespace rra {
+
+template <int D>
+__device__ __forceinline__ void load_kagg_tile(u32x4 (&a)[D / 16], const uint16_t* kbase, int jrow) {
+  const uint16_t* p = kbase + static_cast<int64_t>(jrow) * D;
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(p + kc * 16);
+}
+
+template <int D>
+__device__ __forceinline__ floatx16 tile_mma(const u32x4 (&a)[D / 16], const bf16x8 (&qb)[D / 16]) {
+  floatx16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) acc = mfma32x32x16(as_bf16x8(a[kc]), qb[kc], acc);
+  return acc;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ kagg,
+                                                          float* __restrict__ score, int H, int Hkv,
+                                                          int G, int L, int S, int Ns, int Nb, int n_rt,
+                                                          int nbg, float c) {
+  constexpr int KC = D / 16;
+  const int lane = threadIdx.x;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  int wg = blockIdx.x;
+  const int rt = wg % n_rt;
+  wg /= n_rt;
+  const int bg = wg % nbg;          // b * Hkv + g
+  const int I = Nb - 1 - wg / nbg;  // longest rows first
+  const int b = bg / Hkv;
+  const int g = bg % Hkv;
+
+  const int rho = rt * 32 + col;    // sampled-query slot inside the group
+  const bool valid = rho < G * R;
+  const int hh = valid ? rho / R : 0;
+  const int ii = rho % R;
+  const int h = g * G + hh;
+  const int i = I * R + ii;         // sampled stride
+  const int64_t pos = static_cast<int64_t>(i) * S + (h % S);
+
+  bf16x8 qb[KC];
+  {
+    const uint16_t* qrow = q + ((static_cast<int64_t>(b) * H + h) * L + pos) * D + half * 8;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + kc * 16);
+      qb[kc] = as_bf16x8(w);
+    }
+  }
+  const uint16_t* kbase = kagg + static_cast<int64_t>(bg) * Ns * D + half * 8;
+  const int ntile = ((I + 1) * R + 31) / 32;
+  const int jmax = valid ? i : -1;  // visible strides: j <= i
+
+  // ---- pass 1: row max and denominator (base-2 logits) ----
+  float m = -INFINITY, z = 0.0f;
+  u32x4 a_cur[KC], a_nxt[KC];
+  load_kagg_tile<D>(a_cur, kbase, min(col, Ns - 1));
+  for (int jt = 0; jt < ntile; ++jt) {
+    if (jt + 1 < ntile) load_kagg_tile<D>(a_nxt, kbase, min((jt + 1) * 32 + col, Ns - 1));
+    const floatx16 acc = tile_mma<D>(a_cur, qb);
+    float x[16];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = jt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      x[v] = (j <= jmax) ? acc[v] * c : -INFINITY;
+      tm = fmaxf(tm, x[v]);
+    }
+    if (tm > -INFINITY) {
+      const float mn = fmaxf(m, tm);
+      float zz = z * fast_exp2(m - mn);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) zz += fast_exp2(x[v] - mn);
+      z = zz;
+      m = mn;
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a_cur[kc] = a_nxt[kc];
+  }
+  {
+    const float mo = shfl_xor_f(m, 32);
+    const float zo = shfl_xor_f(z, 32);
+    const float mm = fmaxf(m, mo);
+    float zt = 0.0f;
+    if (m > -INFINITY) zt += z * fast_exp2(m - mm);
+    if (mo > -INFINITY) zt += zo * fast_exp2(mo - mm);
+    m = mm;
+    z = zt;
+  }
+  const float invz = valid ? 1.0f / z : 0.0f;
+  const float inv_r = 1.0f / static_cast<float>(R);
+  float* srow_base = score + (static_cast<int64_t>(b) * H * Nb + I) * Nb;  // + h * Nb * Nb + J
+
+  // ---- pass 2: probabilities pooled into block cells ----
+  load_kagg_tile<D>(a_cur, kbase, min(col, Ns - 1));
+  for (int jt = 0; jt < ntile; ++jt) {
+    if (jt + 1 < ntile) load_kagg_tile<D>(a_nxt, kbase, min((jt + 1) * 32 + col, Ns - 1));
+    const floatx16 acc = tile_mma<D>(a_cur, qb);
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = jt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      p[v] = (j <= jmax) ? fast_exp2(acc[v] * c - m) * invz : 0.0f;
+    }
+    if constexpr (R >= 8) {
+      // A block spans R >= 8 strides: groups of 4 values (v >> 2) in both lane halves.
+      constexpr int NJ = 32 / R;
+      float part[NJ];
+#pragma unroll
+      for (int u = 0; u < NJ; ++u) part[u] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[(8 * (v >> 2)) / R] += p[v];
+#pragma unroll
+      for (int u = 0; u < NJ; ++u) {
+        float t = part[u] + shfl_xor_f(part[u], 32);
+#pragma unroll
+        for (int off = 1; off < R; off <<= 1) t += shfl_xor_f(t, off);
+        part[u] = t;
+      }
+      if (valid && half == 0 && (col % R) == 0) {
+#pragma unroll
+        for (int u = 0; u < NJ; ++u) {
+          const int J = jt * NJ + u;
+          if (J <= I) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+        }
+      }
+    } else {
+      // A block spans R <= 4 strides: each lane half holds whole blocks.
+      constexpr int PER = 4 / R;   // blocks per 4-value group
+      constexpr int NJL = 16 / R;  // blocks per lane
+      float part[NJL];
+#pragma unroll
+      for (int u = 0; u < NJL; ++u) part[u] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) part[(v >> 2) * PER + (v & 3) / R] += p[v];
+#pragma unroll
+      for (int u = 0; u < NJL; ++u) {
+        float t = part[u];
+#pragma unroll
+        for (int off = 1; off < R; off <<= 1) t += shfl_xor_f(t, off);
+        part[u] = t;
+      }
+      if (valid && (col % R) == 0) {
+#pragma unroll
+        for (int u = 0; u < NJL; ++u) {
+          const int so = 8 * (u / PER) + 4 * half + R * (u % PER);  // first stride of the block in the tile
+          const int J = jt * (32 / R) + so / R;
+          if (J <= I) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+        }
+      }
+    }
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a_cur[kc] = a_nxt[kc];
+  }
+
+  // ---- zeros above the diagonal for the heads of this row tile ----
+  constexpr int HPT = 32 / R;  // heads per row tile
+  for (int t = 0; t < HPT; ++t) {
+    const int hz = rt * HPT + t;
+    if (hz >= G) break;
+    float* zrow = srow_base + static_cast<int64_t>(g * G + hz) * Nb * Nb;
+    for (int J = I + 1 + lane; J < Nb; J += 64) zrow[J] = 0.0f;
+  }
+}
+
+template <int D, int R>
+static void launch_bs(const Shape& s, const uint16_t* q, const uint16_t* kagg, float* score, hipStream_t st) {
+  const int n_rt = (s.G * R + 31) / 32;
+  const int nbg = s.Bz * s.Hkv;
+  const int64_t blocks = static_cast<int64_t>(n_rt) * nbg * s.Nb;
+  const float c = s.scale * kLog2e;
+  hipLaunchKernelGGL((block_scores_kernel<D, R>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, st, q, kagg,
+                     score, s.H, s.Hkv, s.G, s.L, s.S, s.Ns, s.Nb, n_rt, nbg, c);
+}
+
+template <int D>
+static void launch_bs_d(const Shape& s, const uint16_t* q, const uint16_t* kagg, float* score, hipStream_t st) {
+  switch (s.r) {
+    case 1: launch_bs<D, 1>(s, q, kagg, score, st); break;
+    case 2: launch_bs<D, 2>(s, q, kagg, score, st); break;
+    case 4: launch_bs<D, 4>(s, q, kagg, score, st); break;
+    case 8: launch_bs<D, 8>(s, q, kagg, score, st); break;
+    case 16: launch_bs<D, 16>(s, q, kagg, score, st); break;
+    default: launch_bs<D, 32>(s, q, kagg, score, st); break;
+  }
+}
+
+int launch_block_scores(const Shape& s, const uint16_t* q, const uint16_t* kagg, float* score, void* stream) {
+  if (static_cast<int64_t>(s.Bz) * s.Nb == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.d == 128)
+    launch_bs_d<128>(s, q, kagg, score, st);
+  else
+    launch_bs_d<64>(s, q, kagg, score, st);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace rra

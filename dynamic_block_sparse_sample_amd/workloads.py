@@ -80,8 +80,8 @@ WORKLOADS = {
 # Headline-workload constants: sink logit bias and slash-band amplitude.
 # Chosen so that the mask density at tau = 0.9 is about one half, the share of
 # blocks the RRAttention page reports computing (§4.2).
-HEADLINE_SINK_BETA = 6.0
-HEADLINE_BAND_PEAK = 8.0
+HEADLINE_SINK_BETA = 4.0
+HEADLINE_BAND_PEAK = 5.0
 
 
 def headline() -> Workload:
@@ -183,3 +183,20 @@ def make_inputs(w: Workload, device="cpu", structure: bool = True):
         return q.to(device), k.to(device), v.to(device)
     return (q.to(torch.bfloat16).to(device), k.to(torch.bfloat16).to(device),
             v.to(torch.bfloat16).to(device))
+
+
+def make_random(batch, num_heads, num_kv_heads, seq_len, head_dim, seed=0, scale=1.0, diag=0.0):
+    """Seeded N(0, scale^2) Q, K, V as bfloat16 on the host.
+
+    diag > 0 adds diag * Q[head 0 of the group] to K, a token-aligned local
+    diagonal that gives the selection some structure.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    q = torch.randn(batch, num_heads, seq_len, head_dim, generator=gen) * scale
+    k = torch.randn(batch, num_kv_heads, seq_len, head_dim, generator=gen) * scale
+    v = torch.randn(batch, num_kv_heads, seq_len, head_dim, generator=gen)
+    if diag:
+        G = num_heads // num_kv_heads
+        k += diag * q[:, ::G]
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)

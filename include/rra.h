@@ -1,0 +1,142 @@
+/*
+ * rra.h -- C ABI of librra.so: RRAttention block-sparse causal prefill
+ * attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described in "RRAttention: Dynamic Block Sparse
+ * Attention via Per-Head Round-Robin Shifts for Long-Context Inference"
+ * (arXiv 2602.05853).  Section references below are to that page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named q, k, v, kagg, score, mask, idx, cnt, out, workspace are
+ *    DEVICE pointers to memory the caller allocated and owns.  The library
+ *    never allocates or frees device memory, never synchronises, and keeps no
+ *    mutable global state, so calls on different streams may run concurrently
+ *    as long as their output buffers do not overlap.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream).  A successful return means the kernels were enqueued.
+ *  - Layouts are dense row-major:
+ *        q, out   [Bz, H,   L, d]     bfloat16
+ *        k, v     [Bz, Hkv, L, d]     bfloat16
+ *        kagg     [Bz, Hkv, Ns, d]    bfloat16, Ns = L / S
+ *        score    [Bz, H, Nb, Nb]     float32,  Nb = L / Bk
+ *        mask     [Bz, H, Nb, Nb]     uint8 (1 = key block selected)
+ *        idx      [Bz, H, Nb, Nb]     int32, first cnt entries of each row valid
+ *        cnt      [Bz, H, Nb]         int32
+ *    Query head h reads KV head h / (H / Hkv) (grouped-query attention).
+ *    Base pointers of bf16/float/int32 arrays must be 16-byte aligned.
+ *  - Every entry point first validates its parameters on the host
+ *    (rra_validate) and its pointers; on failure it returns the status and
+ *    enqueues nothing.  A failed launch returns RRA_ERR_HIP.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef RRA_H_
+#define RRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RRA_ABI_VERSION 1
+
+typedef enum rra_status {
+  RRA_OK = 0,
+  RRA_ERR_INVALID_ARG = 1, /* a parameter or pointer is invalid            */
+  RRA_ERR_UNSUPPORTED = 2, /* valid for the method but not built (shapes)  */
+  RRA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+  RRA_ERR_HIP = 4          /* the HIP runtime reported an error            */
+} rra_status_t;
+
+/* Problem description (§2.1: Q, K of one head are L x d, split into blocks
+ * of Bk tokens, with a finer sampling stride S; §3.3: threshold tau;
+ * causal prefill, §4.1).  Supported: H % Hkv == 0; d in {64, 128};
+ * Bk in {64, 128}; L % Bk == 0; Bk % S == 0 and Bk / S <= 32;
+ * L / Bk <= 4096; 0 < tau <= 1; causal == 1; protect_last in {0, 1}.
+ * batch == 0 or seq_len == 0 is a valid empty problem: every entry point
+ * returns RRA_OK without touching memory. */
+typedef struct rra_params {
+  int32_t batch;        /* Bz                                              */
+  int32_t num_heads;    /* H, query heads                                  */
+  int32_t num_kv_heads; /* Hkv, key/value heads                            */
+  int32_t seq_len;      /* L                                               */
+  int32_t head_dim;     /* d                                               */
+  int32_t stride;       /* S, sampling stride (§2.1)                       */
+  int32_t block;        /* Bk, query and key block size (§2.1's B)         */
+  float tau;            /* Top-tau threshold (§3.3); 1 keeps every block   */
+  int32_t causal;       /* must be 1                                       */
+  int32_t protect_last; /* 1: the last query-block row keeps every causal
+                           key block (§4.3, last query block protection)  */
+  float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim)      */
+} rra_params_t;
+
+/* RRA_ABI_VERSION of the loaded library. */
+int rra_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* rra_status_str(rra_status_t status);
+
+/* Host-only parameter check; makes no HIP call. */
+rra_status_t rra_validate(const rra_params_t* p);
+
+/* Bytes of device workspace rra_estimate needs (*bytes is written). */
+rra_status_t rra_estimate_workspace_size(const rra_params_t* p, size_t* bytes);
+
+/* Round n float32 values to bfloat16, round to nearest even (used when
+ * inputs arrive in float32; the method itself runs on bf16). */
+rra_status_t rra_cast_f32_to_bf16(const float* src, void* dst_bf16, int64_t n, void* stream);
+
+/* Stride key aggregation (§3.2: the sum of the key vectors of each stride,
+ * normalised by 1/S): kagg[b,g,j,:] = bf16_rne( (sum_{t=jS}^{jS+S-1} k[b,g,t,:]) / S ).
+ * The sum is formed exactly (float64) and rounded once to bf16. */
+rra_status_t rra_stride_aggregate(const rra_params_t* p, const void* k, void* kagg, void* stream);
+
+/* Round-robin sampled stride scores, stride softmax and block pooling
+ * (§3.1, §3.2, §2.2 query independence).  For query head h the query of
+ * stride i is taken at position P(i,h) = i*S + (h mod S); its scores
+ * s[i,j] = sm_scale * <q[P(i,h)], kagg[j]> over strides j <= i are softmax
+ * normalised per sampled query, and pooled:
+ *   score[b,h,I,J] = (1/r) * sum_{i in block I} sum_{j in block J, j <= i} p[i,j],
+ * r = Bk / S, so every row sums to 1.  Entries with J > I are written as 0. */
+rra_status_t rra_block_scores(const rra_params_t* p, const void* q, const void* kagg, float* score,
+                              void* stream);
+
+/* Adaptive Top-tau block selection (§3.3; same rule as XAttention's
+ * threshold selection).  For each row (b,h,I): order J in [0, I] by
+ * (score desc, J asc) and keep the shortest prefix whose cumulative score
+ * reaches tau * (row total); keep every J <= I when tau >= 1 or when
+ * protect_last is set and I == Nb - 1.  Writes the whole mask row (0 above
+ * the diagonal), idx[b,h,I,0:cnt] strictly ascending, and cnt[b,h,I]. */
+rra_status_t rra_top_tau(const rra_params_t* p, const float* score, uint8_t* mask, int32_t* idx,
+                         int32_t* cnt, void* stream);
+
+/* The whole estimator: rra_stride_aggregate -> rra_block_scores ->
+ * rra_top_tau.  workspace must hold rra_estimate_workspace_size() bytes
+ * (kagg, and the score matrix when `score` is NULL).  `score` is optional. */
+rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, void* workspace,
+                          size_t workspace_bytes, uint8_t* mask, int32_t* idx, int32_t* cnt,
+                          float* score, void* stream);
+
+/* Block-sparse causal flash attention (§4.1, prefill): for query t of
+ * block I of head h,
+ *   out[b,h,t] = sum_{u in A(t)} softmax_u(sm_scale * q_t . k_u) v_u,
+ *   A(t) = { u <= t : block(u) in idx[b,h,I,0:cnt[b,h,I]] }.
+ * idx rows must be strictly ascending key-block indices in [0, I] with
+ * 1 <= cnt <= I + 1 (rra_top_tau's output satisfies this; other lists are
+ * the caller's responsibility).  bf16 MFMA, float32 accumulation and online
+ * softmax; out is rounded to bf16. */
+rra_status_t rra_sparse_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
+                             const int32_t* idx, const int32_t* cnt, void* out, void* stream);
+
+/* Dense causal flash attention: rra_sparse_attn with every causal key block
+ * selected (the FlashAttention baseline of §4.1), same kernel. */
+rra_status_t rra_dense_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
+                            void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RRA_H_ */

@@ -1,0 +1,100 @@
+"""Shared helpers for the parity tests: oracle parameters, the near-tie rule
+for Top-tau masks, and sampled output checks."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import rra_oracle as orc
+
+# Near-tie tolerance for masks (a cumulative prefix within this of tau, or two
+# masses at the cut within this relative gap, may legitimately be cut either
+# way by float32 vs float64 arithmetic).
+TIE_TOL = 1e-4
+SCORE_ATOL = 1e-5  # block scores, float32 GPU vs float64 oracle
+OUT_ATOL = 1e-2  # attention outputs, bf16 inputs with float32 accumulation
+
+
+def out_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Max error of a bf16 output beyond the rounding of the output itself.
+
+    The library returns bf16, so even a perfect kernel differs from the exact
+    (float64 oracle) value by up to half a bf16 ulp of that value; with
+    unit-variance V that alone exceeds 1e-2 for |out| >= 4.  The tolerance
+    bounds what is left: max(|got - ref| - ulp_bf16(ref) / 2)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    _, ex = np.frexp(np.abs(ref))
+    half_ulp = np.ldexp(1.0, np.maximum(ex - 1, -126) - 8)
+    return float(np.max(np.abs(got - ref) - half_ulp))
+
+
+def oracle_params(w, tau=None, stride=None, protect_last=True) -> orc.Params:
+    t = w.tau if tau is None else tau
+    return orc.Params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim,
+                      w.stride if stride is None else stride, w.block,
+                      float(np.float32(t)), protect_last)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _order(vals):
+    n = vals.size
+    return np.lexsort((np.arange(n), -vals))
+
+
+def compare_masks(gpu_mask, gpu_cnt, gpu_idx, m_oracle, prm: orc.Params, heads=None):
+    """Compare GPU selections with the oracle's, row by row.
+
+    Rows equal to the oracle pass.  A differing row must be a near-tie (an
+    oracle prefix within TIE_TOL of tau, or masses at the cut within TIE_TOL
+    relative) and must still be a valid Top-tau selection under the oracle's
+    masses.  Returns (rows_checked, near_tie_rows, bad_rows)."""
+    B, H, nb, _ = gpu_mask.shape
+    heads = range(H) if heads is None else heads
+    checked = near = 0
+    bad = []
+    for b in range(B):
+        for h in heads:
+            for i in range(nb):
+                checked += 1
+                n = i + 1
+                gsel = np.nonzero(gpu_mask[b, h, i, :n])[0]
+                assert np.all(gpu_mask[b, h, i, n:] == 0), "mask above the diagonal"
+                assert gpu_cnt[b, h, i] == gsel.size, "count does not match the mask"
+                assert np.array_equal(gpu_idx[b, h, i, :gsel.size], gsel), "index list is not the ascending mask"
+                osel = orc.top_tau_row(m_oracle[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1)
+                if np.array_equal(gsel, osel):
+                    continue
+                vals = m_oracle[b, h, i, :n]
+                T = vals.sum()
+                order = _order(vals)
+                csum = np.cumsum(vals[order]) / T
+                ks = osel.size
+                prefix_tie = np.any(np.abs(csum - prm.tau) < TIE_TOL)
+                mass_tie = ks < n and abs(vals[order[ks - 1]] - vals[order[ks]]) < TIE_TOL * vals[order[ks - 1]]
+                if not (prefix_tie or mass_tie):
+                    bad.append((b, h, i, "differs without a near tie"))
+                    continue
+                near += 1
+                gm = vals[gsel].sum()
+                unsel = np.setdiff1d(np.arange(n), gsel)
+                ok = gm >= (prm.tau - TIE_TOL) * T
+                ok &= abs(gsel.size - ks) <= 1
+                if unsel.size:
+                    ok &= vals[gsel].min() >= vals[unsel].max() * (1 - TIE_TOL) - 1e-12
+                ok &= gm - vals[gsel].min() < (prm.tau + TIE_TOL) * T
+                if not ok:
+                    bad.append((b, h, i, "near tie but not a valid Top-tau set"))
+    return checked, near, bad
+
+
+def check_output_rows(out_gpu, q, k, v, mask, prm: orc.Params, rows):
+    """Max-abs error of GPU output rows against the oracle on the given mask."""
+    worst = 0.0
+    for (b, h, i) in rows:
+        ref = orc.attention_rows(q, k, v, mask, prm, b, h, i)
+        got = to_f64(out_gpu[b, h, i * prm.block:(i + 1) * prm.block])
+        worst = max(worst, out_err(got, ref))
+    return worst

@@ -1,0 +1,144 @@
+"""The C ABI library loads on a machine without a GPU, exports every symbol
+the header declares, and its host-side checks return the documented status
+codes.  Nothing here launches a kernel: every call below fails validation
+before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_sample_amd as rra
+from dynamic_block_sparse_sample_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rra.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="librra.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(rra_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = header_functions()
+    assert len(names) == 11, names
+    lib = rra.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_params_struct_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct rra_params \{(.*?)\} rra_params_t;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [f for _, f in fields] == [n for n, _ in rra.Params._fields_]
+    for (ty, _), (_, cty) in zip(fields, rra.Params._fields_):
+        assert cty == (ctypes.c_int32 if ty == "int32_t" else ctypes.c_float)
+    assert ctypes.sizeof(rra.Params) == 44
+
+
+def test_abi_version_and_status_strings():
+    assert rra.lib().rra_abi_version() == 1
+    for code in range(5):
+        assert rra.status_str(code).startswith("RRA_")
+    assert rra.status_str(99) == "RRA_ERR_UNKNOWN"
+
+
+def P(**kw):
+    base = dict(batch=1, num_heads=32, num_kv_heads=8, seq_len=8192, head_dim=128, stride=16, block=128,
+                tau=0.9, protect_last=True, sm_scale=0.0, causal=True)
+    base.update(kw)
+    return rra.make_params(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    (dict(head_dim=64, block=64, stride=8, seq_len=1024, num_heads=4, num_kv_heads=4), 0),
+    (dict(num_heads=28, num_kv_heads=4, seq_len=65536, tau=0.95), 0),
+    (dict(stride=4), 0),
+    (dict(stride=128), 0),
+    (dict(tau=1.0), 0),
+    (dict(batch=0), 0),  # empty problem: valid no-op
+    (dict(seq_len=0), 0),
+    (dict(batch=-1), 1),
+    (dict(num_heads=30), 1),  # H % Hkv != 0
+    (dict(tau=0.0), 1),
+    (dict(tau=1.5), 1),
+    (dict(tau=float("nan")), 1),
+    (dict(sm_scale=float("inf")), 1),
+    (dict(stride=3), 1),  # Bk % S != 0
+    (dict(stride=0), 1),
+    (dict(num_kv_heads=0), 1),
+    (dict(head_dim=96), 2),
+    (dict(block=256, stride=16), 2),
+    (dict(seq_len=8000), 2),  # L % Bk != 0
+    (dict(stride=2), 2),  # Bk / S = 64 > 32
+    (dict(causal=False), 2),
+    (dict(seq_len=128 * 4097), 2),  # more than 4096 blocks
+])
+def test_validate_status_codes(kw, code):
+    assert rra.validate(P(**kw)) == code
+
+
+def test_protect_last_must_be_boolean():
+    p = P()
+    p.protect_last = 2
+    assert rra.validate(p) == 1
+
+
+def test_workspace_size_formula():
+    p = P()
+    nb, ns = 8192 // 128, 8192 // 16
+    kagg = 1 * 8 * ns * 128 * 2
+    score = 1 * 32 * nb * nb * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert rra.workspace_size(p) == r256(kagg) + r256(score)
+    assert rra.workspace_size(P(batch=0)) == 0
+    with pytest.raises(rra.RRAError):
+        rra.workspace_size(P(head_dim=96))
+
+
+def test_entry_points_reject_null_and_misaligned_pointers_without_launching():
+    lib = rra.lib()
+    p = P()
+    null = None
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    s = None
+    by = ctypes.byref
+    assert lib.rra_stride_aggregate(by(p), null, fake, s) == 1
+    assert lib.rra_stride_aggregate(by(p), odd, fake, s) == 1
+    assert lib.rra_block_scores(by(p), fake, null, fake, s) == 1
+    assert lib.rra_top_tau(by(p), fake, fake, null, fake, s) == 1
+    assert lib.rra_sparse_attn(by(p), fake, fake, fake, fake, null, fake, s) == 1
+    assert lib.rra_dense_attn(by(p), fake, fake, fake, odd, s) == 1
+    assert lib.rra_cast_f32_to_bf16(null, fake, 16, s) == 1
+    assert lib.rra_cast_f32_to_bf16(fake, fake, -1, s) == 1
+    assert lib.rra_cast_f32_to_bf16(null, null, 0, s) == 0  # nothing to do
+    # workspace missing / too small
+    assert lib.rra_estimate(by(p), fake, fake, null, 0, fake, fake, fake, null, s) == 3
+    need = rra.workspace_size(p)
+    assert lib.rra_estimate(by(p), fake, fake, fake, need - 1, fake, fake, fake, null, s) == 3
+    # invalid parameters win over everything else
+    bad = P(head_dim=96)
+    assert lib.rra_estimate(by(bad), fake, fake, fake, 1 << 40, fake, fake, fake, null, s) == 2
+    assert lib.rra_dense_attn(None, fake, fake, fake, fake, s) == 1
+
+
+def test_empty_problem_is_a_no_op_even_with_null_pointers():
+    lib = rra.lib()
+    p = P(batch=0)
+    by = ctypes.byref
+    assert lib.rra_estimate(by(p), None, None, None, 0, None, None, None, None, None) == 0
+    assert lib.rra_sparse_attn(by(p), None, None, None, None, None, None, None) == 0
+    assert lib.rra_dense_attn(by(p), None, None, None, None, None) == 0
+    assert lib.rra_stride_aggregate(by(p), None, None, None) == 0
+    assert lib.rra_block_scores(by(p), None, None, None, None) == 0
+    assert lib.rra_top_tau(by(p), None, None, None, None, None) == 0
