@@ -24,6 +24,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+COPY_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
 
 
 def log(*a):
@@ -98,6 +99,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
+                    help="profile: one estimate, --steps sparse-attention launches, one dense launch and a "
+                         "256 MiB device copy (HBM-counter calibration); prints a short summary only")
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic_sparse_attn_llama_128k.json"))
     args = ap.parse_args(argv)
@@ -136,6 +140,19 @@ def main(argv=None) -> int:
     def step():
         rra.estimate(p, qd, kd, workspace=ws, out=sel)
         rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)
+
+    if args.mode == "profile":
+        rra.estimate(p, qd, kd, workspace=ws, out=sel)
+        for _ in range(args.steps):
+            rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)
+        rra.dense_attn(p, qd, kd, vd, out=dense_out)
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # calibration: reads and writes exactly COPY_BYTES
+        torch.cuda.synchronize()
+        log(f"[bench] profile run done: sum(cnt) = {int(sel.cnt.sum())}, copy {COPY_BYTES} B")
+        return 0
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
