@@ -3,21 +3,36 @@
 // kernel with every causal block listed).
 //
 // One workgroup per (batch, query head h, query block I) with BLK/32 waves;
-// wave w owns 32 queries.  For each listed key block J the workgroup stages
-// K[J] row-major and V[J] transposed into LDS, then every wave computes
-//   S^T = K_J Q^T          (v_mfma_f32_32x32x16_bf16, A = 32 keys, B = 32 queries)
-// so each lane holds one query (lane & 31) and 16 of every 32 keys.  The
-// online softmax (base 2, float32) needs only in-lane reductions plus one
-// exchange with lane ^ 32.  The probabilities, rounded to bf16, are already in
-// the B-operand layout of the second product
-//   O^T += V_J^T P^T       (A = 32 channels x 16 keys read from the V^T tile)
-// once the keys of the contraction are enumerated in the order the first
-// product left them in the lanes (a permutation of the summation index).
+// wave w owns 32 queries.  Key blocks are consumed in 64-key sub-tiles.
+//
+// Data movement: K and V sub-tiles (64 keys x d, row-major) are copied from
+// global memory straight into LDS with global_load_lds_dwordx4 (lane l's 16
+// bytes land at LDS base + 16 l), double-buffered: the copy of sub-tile s+1 is
+// in flight while sub-tile s is computed, and no VGPRs are spent on staging.
+// Each 256-byte key row keeps its sixteen 16-byte chunks XOR-swizzled by a
+// function of the row, chosen so that both LDS read patterns below are free of
+// bank conflicts with 32 or 64 banks.
+//
+// Compute per sub-tile and wave:
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, A = 32 keys (ds_read_b128 from
+//                  LDS), B = 32 queries (registers).  Each lane then holds one
+//                  query (lane & 31) and 16 of every 32 keys, so the online
+//                  softmax (base 2, float32) is in-lane plus one exchange with
+//                  lane ^ 32.
+//   O^T += V^T P^T A = 32 channels x 16 keys, read with ds_read_b64_tr_b16:
+//                  in each 16-lane group, lane i receives element i mod 4 of
+//                  the 8-byte rows addressed by lanes i/4 + 4m (m = 0..3), i.e.
+//                  4 consecutive keys of one channel; B = the bf16
+//                  probabilities, already in place once the contraction's keys
+//                  are enumerated in the order the first product left them.
+// The running max is exact (the largest probability of a row is exactly 1, so
+// the dominant term of a peaked row carries no bf16 rounding); O and l are
+// rescaled only on sub-tiles where some row's max increased.
 //
 // Work order: longest rows (largest I) first; when the KV groups divide
 // evenly over the 8 XCDs, the workgroups of one KV group are mapped to one XCD
 // (workgroup w runs on XCD w mod 8) so the heads of a group and neighbouring
-// query blocks share K/V tiles in that XCD's L2.
+// query blocks share K/V in that XCD's L2.
 #include <cmath>
 
 #include "../rra_internal.h"
@@ -25,17 +40,81 @@
 
 namespace rra {
 
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
 template <int D, int BLK>
 struct FaCfg {
-  static constexpr int NW = BLK / 32;  // waves, 32 queries each
+  static constexpr int NW = BLK / 32;          // waves, 32 queries each
   static constexpr int NT = NW * 64;
-  static constexpr int KP = D + 8;     // K tile pitch (bf16): rows 4 banks apart
-  static constexpr int VP = BLK + 4;   // V^T tile pitch (bf16): rows 2 banks apart
-  static constexpr int KC = D / 16;    // MFMA k-chunks of Q K^T
-  static constexpr int ST = BLK / 32;  // 32-key tiles of S^T
-  static constexpr int CT = D / 32;    // 32-channel tiles of O^T
-  static constexpr int LDS_BYTES = (BLK * KP + D * VP) * 2;
+  static constexpr int KT = 64;                // keys per sub-tile
+  static constexpr int SUB = BLK / KT;         // sub-tiles per key block
+  static constexpr int RC = D / 8;             // 16-byte chunks per key row
+  static constexpr int ROWB = D * 2;           // bytes per key row
+  static constexpr int TILE = KT * ROWB;       // bytes of one K (or V) sub-tile
+  static constexpr int STAGE = 2 * TILE;       // K then V
+  static constexpr int NINST = KT * RC / 64;   // 1 KB copy instructions per sub-tile (each of K, V)
+  static constexpr int IPW = NINST / NW;       // ... per wave
+  static constexpr int ROWS_PER_INST = 64 / RC;
+  static constexpr int KC = D / 16;            // MFMA k-chunks of Q K^T
+  static constexpr int CT = D / 32;            // 32-channel tiles of O^T
+  static_assert(NINST % NW == 0, "copy split");
 };
+
+// Chunk swizzle of key row r (bits: r1 -> 3, r0 -> 2, r1^r3 -> 1, r2 -> 0).
+__device__ __forceinline__ int swz(int r) {
+  return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | ((((r >> 1) ^ (r >> 3)) & 1) << 1) | ((r >> 2) & 1);
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// 16 bytes per lane from global memory (gbase + voff) into LDS at
+// lds + 16 * lane (global_load_lds_dwordx4, saddr form).  Issued from inline
+// asm so that the compiler does not tie later LDS reads of the other pipeline
+// stage to this copy with a full vmcnt wait; completion is tracked explicitly
+// with wait_vmcnt.  m0 (the LDS base) is saved and restored.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* gbase, int voff, uint32_t lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Workgroup barrier that does not wait for global loads in flight (the copy
+// of the next sub-tile).  The only LDS writes in the loop are those copies; a
+// wave's own copies of the current sub-tile are completed by wait_vmcnt before
+// it arrives, so after the barrier every wave's copies have landed.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Barrier after this wave's LDS reads of a stage have completed (lgkmcnt(0),
+// vmcnt untouched), so no wave refills the stage while another reads it.
+__device__ __forceinline__ void lds_reads_done_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 enum WorkMap : int { kMapPlain = 0, kMapXcdGroups = 1, kMapXcdSplit = 2 };
 
@@ -45,9 +124,10 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
     int Hkv, int G, int L, int Nb, float c, int map_mode) {
   using C = FaCfg<D, BLK>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[C::LDS_BYTES / 2];
-  uint16_t* Ks = lds;                // [BLK][KP]
-  uint16_t* Vt = lds + BLK * C::KP;  // [D][VP]
+  // Two pipeline stages in distinct LDS objects, so the compiler can tell the
+  // reads of one stage from the copy in flight into the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
 
   // ---- work item ----
   const int nbg = static_cast<int>(gridDim.x / (static_cast<unsigned>(G) * Nb));
@@ -86,7 +166,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   const int64_t row = (static_cast<int64_t>(b) * H + h) * Nb + I;
 
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -100,151 +180,180 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) qb[kc] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kc * 16));
   }
+  // Complete the Q loads now (an empty asm consuming the registers makes the
+  // compiler wait here): inside the loop vmcnt also counts the K/V copies in
+  // flight, so a compiler-placed wait for Q there would drain the prefetch.
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) asm volatile("" ::"v"(qb[kc]));
 
   floatx16 o[C::CT];
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[ct][e] = 0.0f;
-  float m = -INFINITY;
-  float l = 0.0f;
+  float m = -INFINITY;  // running max (base-2 logits)
+  float l = 0.0f;       // this lane half's share of the denominator
 
-  const int n = (idx == nullptr) ? I + 1 : cnt[row];
-  const int32_t* list = (idx == nullptr) ? nullptr : idx + row * Nb;
-  const uint16_t* kbase = k + static_cast<int64_t>(bg) * L * D;
-  const uint16_t* vbase = v + static_cast<int64_t>(bg) * L * D;
+  // The index list is read-only for the whole kernel: read it through the
+  // constant address space so the uniform loads are scalar (s_load).
+  const int nblk = (idx == nullptr) ? I + 1 : ((const_i32_ptr)(cnt))[row];
+  const int n_sub = nblk * C::SUB;
+  const_i32_ptr list = (idx == nullptr) ? nullptr : ((const_i32_ptr)(idx)) + row * Nb;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + static_cast<int64_t>(bg) * L * C::ROWB;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(v) + static_cast<int64_t>(bg) * L * C::ROWB;
 
-  for (int it = 0; it < n; ++it) {
-    const int J = (list == nullptr) ? it : list[it];
-    const uint16_t* kblk = kbase + static_cast<int64_t>(J) * BLK * D;
-    const uint16_t* vblk = vbase + static_cast<int64_t>(J) * BLK * D;
+  // Per-lane pieces of the copy addresses: lane -> (row inside the instruction's rows, chunk slot).
+  const int cp_row = lane / C::RC;
+  const int cp_slot = lane % C::RC;
 
-    // ---- stage K (row-major) and V (transposed) into LDS ----
-    constexpr int KITEMS = BLK * D / 8;         // 16-byte chunks of the K block
-    constexpr int KPER = KITEMS / C::NT;
-    constexpr int VITEMS = (BLK / 4) * (D / 8);  // 4 keys x 8 channels each
-    constexpr int VPER = VITEMS / C::NT;
-    u32x4 kr[KPER];
-    u32x4 vr[VPER][4];
+  auto block_of = [&](int s) { return (list == nullptr) ? s / C::SUB : list[s / C::SUB]; };
+  // Global byte offset (inside a sub-tile) of the 16 bytes this lane copies in
+  // each of its copy instructions; the same for K and V.
+  int goff[C::IPW];
 #pragma unroll
-    for (int e = 0; e < KPER; ++e) {
-      const int item = tid + e * C::NT;
-      const int rr = item / (D / 8);
-      const int c8 = item % (D / 8);
-      kr[e] = *reinterpret_cast<const u32x4*>(kblk + rr * D + c8 * 8);
+  for (int i = 0; i < C::IPW; ++i) {
+    const int inst = wv * C::IPW + i;
+    const int r = inst * C::ROWS_PER_INST + cp_row;
+    const int chunk = cp_slot ^ (swz(r) & (C::RC - 1));
+    goff[i] = r * C::ROWB + chunk * 16;
+  }
+  auto issue = [&](int s, int J, uint8_t* kl) {
+    const int64_t key0 = static_cast<int64_t>(J) * BLK + (s % C::SUB) * C::KT;
+    const uint8_t* kg = kbase + key0 * C::ROWB;
+    const uint8_t* vg = vbase + key0 * C::ROWB;
+    const uint32_t lk = lds_addr(kl) + wv * C::IPW * 1024;
+#pragma unroll
+    for (int i = 0; i < C::IPW; ++i) {
+      copy16_to_lds(kg, goff[i], lk + i * 1024);
+      copy16_to_lds(vg, goff[i], lk + C::TILE + i * 1024);
     }
-#pragma unroll
-    for (int e = 0; e < VPER; ++e) {
-      const int item = tid + e * C::NT;
-      const int kg = (item & 15) + 16 * (item / (16 * (D / 8)));
-      const int c8 = (item >> 4) % (D / 8);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vr[e][kk] = *reinterpret_cast<const u32x4*>(vblk + (4 * kg + kk) * D + c8 * 8);
-    }
-    __syncthreads();  // every wave is done reading the previous tiles
-#pragma unroll
-    for (int e = 0; e < KPER; ++e) {
-      const int item = tid + e * C::NT;
-      const int rr = item / (D / 8);
-      const int c8 = item % (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + rr * C::KP + c8 * 8) = kr[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VPER; ++e) {
-      const int item = tid + e * C::NT;
-      const int kg = (item & 15) + 16 * (item / (16 * (D / 8)));
-      const int c8 = (item >> 4) % (D / 8);
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        // channel c8*8+ch of keys 4kg..4kg+3 -> one 8-byte row segment of V^T
-        const int wd = ch >> 1;
-        const bool hi = ch & 1;
-        uint32_t k0 = hi ? (vr[e][0][wd] >> 16) : (vr[e][0][wd] & 0xffffu);
-        uint32_t k1 = hi ? (vr[e][1][wd] >> 16) : (vr[e][1][wd] & 0xffffu);
-        uint32_t k2 = hi ? (vr[e][2][wd] >> 16) : (vr[e][2][wd] & 0xffffu);
-        uint32_t k3 = hi ? (vr[e][3][wd] >> 16) : (vr[e][3][wd] & 0xffffu);
-        u32x2 pk;
-        pk[0] = k0 | (k1 << 16);
-        pk[1] = k2 | (k3 << 16);
-        *reinterpret_cast<u32x2*>(Vt + (c8 * 8 + ch) * C::VP + 4 * kg) = pk;
-      }
-    }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T ----
-    floatx16 s[C::ST];
+  // LDS read offsets that do not depend on the sub-tile.
+  int koff[C::KC];  // S^T A operand: key row 32t + col (t added later), chunk 2kc + half
+  {
+    const int sw = swz(col) & (C::RC - 1);
 #pragma unroll
-    for (int t = 0; t < C::ST; ++t) {
+    for (int kc = 0; kc < C::KC; ++kc) koff[kc] = col * C::ROWB + (((2 * kc + half) ^ sw) * 16);
+  }
+  // V^T A operand via transposed reads: key row kb0 + s/4 with kb0 = 32t + 16u + 4 half (+8),
+  // channel 32 ct + 16 g16 + 4 (s % 4) (+ lane's element).
+  const int s16 = lane & 15;
+  const int g16 = (lane >> 4) & 1;
+  int voff[2][C::CT];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[t][e] = 0.0f;
+  for (int e8 = 0; e8 < 2; ++e8) {
+    const int r = 4 * half + 8 * e8 + (s16 >> 2);  // row bits below 16 (t, u add multiples of 16)
+    const int sw = swz(r) & (C::RC - 1);
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) {
+      const int chunk = 4 * ct + 2 * g16 + ((s16 & 3) >> 1);
+      voff[e8][ct] = r * C::ROWB + ((chunk ^ sw) * 16) + (s16 & 1) * 8;
+    }
+  }
+
+  // J of the sub-tile being computed is carried from the step that issued its
+  // copy, so the compute path has no scalar loads.
+  int J = (n_sub > 0) ? block_of(0) : 0;
+  if (n_sub > 0) issue(0, J, stage0);
+
+  // One sub-tile: start the copy of sub-tile s+1 into `nxt`, wait for this
+  // wave's copies of sub-tile s (in `cur`), barrier, compute, barrier.
+  auto step = [&](int s, const uint8_t* cur, uint8_t* nxt) {
+    int J_next = J;
+    if (s + 1 < n_sub) {
+      J_next = block_of(s + 1);
+      issue(s + 1, J_next, nxt);
+      wait_vmcnt<2 * C::IPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // sub-tile s is in LDS for every wave
+
+    const uint8_t* Ks = cur;
+    const uint8_t* Vs = cur + C::TILE;
+    const int key_base = (s % C::SUB) * C::KT;  // key offset of this sub-tile inside block J
+    // ---- S^T = K Q^T over 64 keys ----
+    floatx16 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[t][e] = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (32 * t + col) * C::KP + kc * 16 + half * 8);
-        s[t] = mfma32x32x16(as_bf16x8(a), qb[kc], s[t]);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + koff[kc] + 32 * t * C::ROWB);
+        st[t] = mfma32x32x16(as_bf16x8(a), qb[kc], st[t]);
       }
     }
 
-    // ---- online softmax (base 2) ----
-    const bool diag = (J == I);
+    // ---- causal mask on the diagonal block, row max ----
+    if (J == I) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key_local = key_base + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+          if (key_local > q_local) st[t][e] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < C::ST; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[t][e] * c;
-        if (diag) {
-          const int key_local = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key_local > q_local) x = -INFINITY;
-        }
-        s[t][e] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[t][e]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+    const bool raise = mx > m;  // m = -inf on the first sub-tile
+    if (__any(raise)) {
+      const float m_new = raise ? mx : m;
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
+      m = m_new;
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    l *= alpha;
-#pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
-    m = m_new;
 
-    u32x4 pb[C::ST][2];
+    // ---- probabilities (bf16, B operand of the second product) ----
+    u32x4 pb[2][2];
 #pragma unroll
-    for (int t = 0; t < C::ST; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(s[t][8 * u + 2 * e] - m_new);
-          const float p1 = fast_exp2(s[t][8 * u + 2 * e + 1] - m_new);
+          const float p0 = fast_exp2(fmaf(st[t][8 * u + 2 * e], c, -m));
+          const float p1 = fast_exp2(fmaf(st[t][8 * u + 2 * e + 1], c, -m));
           l += p0 + p1;
           pb[t][u][e] = pack_bf16x2(p0, p1);
         }
-      }
-    }
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int ct = 0; ct < C::CT; ++ct) {
-      const uint16_t* vrow = Vt + (32 * ct + col) * C::VP + 4 * half;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < C::ST; ++t) {
+      for (int u = 0; u < 2; ++u) {
+        const int rowoff = (32 * t + 16 * u) * C::ROWB;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 32 * t + 16 * u);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 32 * t + 16 * u + 8);
+        for (int ct = 0; ct < C::CT; ++ct) {
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(Vs + rowoff + voff[0][ct]));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(Vs + rowoff + voff[1][ct]));
           u32x4 a;
-          a[0] = lo[0];
-          a[1] = lo[1];
-          a[2] = hi[0];
-          a[3] = hi[1];
+          a[0] = static_cast<uint16_t>(lo[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16);
+          a[1] = static_cast<uint16_t>(lo[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16);
+          a[2] = static_cast<uint16_t>(hi[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16);
+          a[3] = static_cast<uint16_t>(hi[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16);
           o[ct] = mfma32x32x16(as_bf16x8(a), as_bf16x8(pb[t][u]), o[ct]);
         }
       }
-    }
+    lds_reads_done_barrier();  // every wave is done with this stage before it is refilled
+    J = J_next;
+  };
+  for (int s = 0; s < n_sub; s += 2) {
+    step(s, stage0, stage1);
+    if (s + 1 < n_sub) step(s + 1, stage1, stage0);
   }
 
   // ---- normalise and store: lane holds 4 consecutive channels per group ----
