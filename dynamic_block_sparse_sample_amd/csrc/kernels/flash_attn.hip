@@ -29,10 +29,10 @@
 // the dominant term of a peaked row carries no bf16 rounding); O and l are
 // rescaled only on sub-tiles where some row's max increased.
 //
-// Work order: longest rows (largest I) first; when the KV groups divide
-// evenly over the 8 XCDs, the workgroups of one KV group are mapped to one XCD
-// (workgroup w runs on XCD w mod 8) so the heads of a group and neighbouring
-// query blocks share K/V in that XCD's L2.
+// Work order: KV groups in phases small enough for the memory-side cache;
+// inside a phase longest rows (largest I) first, each group's workgroups on a
+// fixed set of XCDs (workgroup w runs on XCD w mod 8), the heads of a group
+// adjacent so that they stream the same K/V through one L2.
 #include <cmath>
 
 #include "../rra_internal.h"
@@ -116,13 +116,11 @@ __device__ __forceinline__ void lds_reads_done_barrier() {
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
-enum WorkMap : int { kMapPlain = 0, kMapXcdGroups = 1, kMapXcdSplit = 2 };
-
 template <int D, int BLK>
 __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
-    int Hkv, int G, int L, int Nb, float c, int map_mode) {
+    int Hkv, int G, int L, int Nb, float c, int gp) {
   using C = FaCfg<D, BLK>;
   // Two pipeline stages in distinct LDS objects, so the compiler can tell the
   // reads of one stage from the copy in flight into the other.
@@ -130,28 +128,25 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
 
   // ---- work item ----
-  const int nbg = static_cast<int>(gridDim.x / (static_cast<unsigned>(G) * Nb));
+  // Workgroup w runs on XCD w mod 8.  The KV groups are processed in phases of
+  // `gp` groups (their K and V fit the memory-side cache together); inside a
+  // phase XCD x takes group x mod gp and every (8/gp)-th query block, longest
+  // rows first, the heads of a group next to each other.
+  const int nbg = static_cast<int>(gridDim.x / (static_cast<unsigned>(G) * Nb));  // Bz * Hkv
   int bg, hh, I;
   {
     const int w = blockIdx.x;
-    if (map_mode == kMapXcdGroups) {
-      const int xcd = w & 7;
-      int slot = w >> 3;
-      const int per = nbg >> 3;
+    if (gp > 0) {
+      const int phase_items = gp * G * Nb;
+      const int ph = w / phase_items;
+      const int r = w % phase_items;
+      const int xcd = r & 7;
+      int slot = r >> 3;
+      const int split = 8 / gp;
       hh = slot % G;
       slot /= G;
-      const int kq = slot % per;
-      I = Nb - 1 - slot / per;
-      bg = xcd + 8 * kq;
-    } else if (map_mode == kMapXcdSplit) {
-      const int xcd = w & 7;
-      int slot = w >> 3;
-      const int split = 8 / nbg;
-      bg = xcd % nbg;
-      const int part = xcd / nbg;
-      hh = slot % G;
-      slot /= G;
-      I = Nb - 1 - (slot * split + part);
+      I = Nb - 1 - (slot * split + xcd / gp);
+      bg = ph * gp + xcd % gp;
     } else {
       int t = w;
       hh = t % G;
@@ -192,7 +187,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[ct][e] = 0.0f;
   float m = -INFINITY;  // running max (base-2 logits)
-  float l = 0.0f;       // this lane half's share of the denominator
+  float l = 0.0f;       // this lane half's share of the denominator (sum of the bf16 p)
 
   // The index list is read-only for the whole kernel: read it through the
   // constant address space so the uniform loads are scalar (s_load).
@@ -324,8 +319,8 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
         for (int e = 0; e < 4; ++e) {
           const float p0 = fast_exp2(fmaf(st[t][8 * u + 2 * e], c, -m));
           const float p1 = fast_exp2(fmaf(st[t][8 * u + 2 * e + 1], c, -m));
-          l += p0 + p1;
           pb[t][u][e] = pack_bf16x2(p0, p1);
+          l = add_bf16x2(pb[t][u][e], l);  // the denominator sums the same rounded p as V^T P^T
         }
 
     // ---- O^T += V^T P^T ----
@@ -372,11 +367,18 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   }
 }
 
-static int work_map_mode(const Shape& s) {
+// Groups per phase of the work order: the largest gp in {8, 4, 2, 1} that
+// divides the group count, splits the query blocks evenly over 8/gp XCDs, and
+// keeps gp groups' K and V within kPhaseBytes.  0 = plain order.
+constexpr int64_t kPhaseBytes = int64_t(128) << 20;
+
+static int phase_groups(const Shape& s) {
   const int nbg = s.Bz * s.Hkv;
-  if (nbg % 8 == 0) return kMapXcdGroups;
-  if (8 % nbg == 0 && s.Nb % (8 / nbg) == 0) return kMapXcdSplit;
-  return kMapPlain;
+  const int64_t kv_bytes = int64_t(2) * s.L * s.d * 2;
+  for (int gp = 8; gp >= 1; gp >>= 1) {
+    if (nbg % gp == 0 && s.Nb % (8 / gp) == 0 && gp * kv_bytes <= kPhaseBytes) return gp;
+  }
+  return s.Nb % 8 == 0 ? 1 : 0;  // one group per phase even above the budget
 }
 
 template <int D, int BLK>
@@ -384,7 +386,7 @@ static void launch_fa(const Shape& s, const uint16_t* q, const uint16_t* k, cons
                       const int32_t* cnt, uint16_t* out, hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
   hipLaunchKernelGGL((flash_attn_kernel<D, BLK>), dim3(static_cast<unsigned>(blocks)), dim3(FaCfg<D, BLK>::NT), 0,
-                     st, q, k, v, idx, cnt, out, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, work_map_mode(s));
+                     st, q, k, v, idx, cnt, out, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, phase_groups(s));
 }
 
 int launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
