@@ -7,24 +7,30 @@
 //
 // Data movement: K and V sub-tiles (64 keys x d, row-major) are copied from
 // global memory straight into LDS with global_load_lds_dwordx4 (lane l's 16
-// bytes land at LDS base + 16 l), double-buffered: the copy of sub-tile s+1 is
-// in flight while sub-tile s is computed, and no VGPRs are spent on staging.
-// Each 256-byte key row keeps its sixteen 16-byte chunks XOR-swizzled by a
-// function of the row, chosen so that both LDS read patterns below are free of
-// bank conflicts with 32 or 64 banks.
+// bytes land at LDS base + 16 l); no VGPRs are spent on staging.  K and V each
+// have a ring of two LDS buffers and K runs one sub-tile ahead of V, so in
+// iteration s the copies of V(s+1) and K(s+2) are in flight while the MFMA
+// unit computes S(s+1) = K(s+1) Q^T and the VALU turns S(s) into
+// probabilities, followed by O += V(s) P(s).  Each 256-byte key row keeps its
+// sixteen 16-byte chunks XOR-swizzled by a function of the row, chosen so
+// that both LDS read patterns below are free of bank conflicts with 32 or 64
+// banks.
 //
 // Compute per sub-tile and wave:
 //   S^T = K Q^T    v_mfma_f32_32x32x16_bf16, A = 32 keys (ds_read_b128 from
 //                  LDS), B = 32 queries (registers).  Each lane then holds one
 //                  query (lane & 31) and 16 of every 32 keys, so the online
 //                  softmax (base 2, float32) is in-lane plus one exchange with
-//                  lane ^ 32.
+//                  lane ^ 32 (v_permlane32_swap).
 //   O^T += V^T P^T A = 32 channels x 16 keys, read with ds_read_b64_tr_b16:
 //                  in each 16-lane group, lane i receives element i mod 4 of
 //                  the 8-byte rows addressed by lanes i/4 + 4m (m = 0..3), i.e.
 //                  4 consecutive keys of one channel; B = the bf16
 //                  probabilities, already in place once the contraction's keys
 //                  are enumerated in the order the first product left them.
+// The 16 MFMAs of S(s+1) are issued in chunks, each followed by one pair of
+// probabilities of S(s) and the LDS read of a K fragment four MFMAs ahead;
+// sched_barrier keeps that order so MFMA and VALU work overlap in one wave.
 // The running max is exact (the largest probability of a row is exactly 1, so
 // the dominant term of a peaked row carries no bf16 rounding); O and l are
 // rescaled only on sub-tiles where some row's max increased.
@@ -122,10 +128,12 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
     int Hkv, int G, int L, int Nb, float c, int gp) {
   using C = FaCfg<D, BLK>;
-  // Two pipeline stages in distinct LDS objects, so the compiler can tell the
-  // reads of one stage from the copy in flight into the other.
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE];
+  // K and V rings of two sub-tiles each (K(t) in kb[t & 1], V(t) in vb[t & 1]),
+  // in distinct LDS objects so every access names its buffer statically.
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[C::TILE];
 
   // ---- work item ----
   // Workgroup w runs on XCD w mod 8.  The KV groups are processed in phases of
@@ -212,16 +220,13 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     const int chunk = cp_slot ^ (swz(r) & (C::RC - 1));
     goff[i] = r * C::ROWB + chunk * 16;
   }
-  auto issue = [&](int s, int J, uint8_t* kl) {
-    const int64_t key0 = static_cast<int64_t>(J) * BLK + (s % C::SUB) * C::KT;
-    const uint8_t* kg = kbase + key0 * C::ROWB;
-    const uint8_t* vg = vbase + key0 * C::ROWB;
-    const uint32_t lk = lds_addr(kl) + wv * C::IPW * 1024;
+  // Copy sub-tile t of K or V (block J) into an LDS buffer: IPW instructions per wave.
+  auto copy_tile = [&](const uint8_t* base, int t, int J, uint8_t* buf) {
+    const int64_t key0 = static_cast<int64_t>(J) * BLK + (t % C::SUB) * C::KT;
+    const uint8_t* gtile = base + key0 * C::ROWB;
+    const uint32_t l0 = lds_addr(buf) + wv * C::IPW * 1024;
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) {
-      copy16_to_lds(kg, goff[i], lk + i * 1024);
-      copy16_to_lds(vg, goff[i], lk + C::TILE + i * 1024);
-    }
+    for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gtile, goff[i], l0 + i * 1024);
   };
 
   // LDS read offsets that do not depend on the sub-tile.
@@ -247,112 +252,170 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     }
   }
 
-  // J of the sub-tile being computed is carried from the step that issued its
-  // copy, so the compute path has no scalar loads.
-  int J = (n_sub > 0) ? block_of(0) : 0;
-  if (n_sub > 0) issue(0, J, stage0);
-
-  // One sub-tile: start the copy of sub-tile s+1 into `nxt`, wait for this
-  // wave's copies of sub-tile s (in `cur`), barrier, compute, barrier.
-  auto step = [&](int s, const uint8_t* cur, uint8_t* nxt) {
-    int J_next = J;
-    if (s + 1 < n_sub) {
-      J_next = block_of(s + 1);
-      issue(s + 1, J_next, nxt);
-      wait_vmcnt<2 * C::IPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // sub-tile s is in LDS for every wave
-
-    const uint8_t* Ks = cur;
-    const uint8_t* Vs = cur + C::TILE;
-    const int key_base = (s % C::SUB) * C::KT;  // key offset of this sub-tile inside block J
-    // ---- S^T = K Q^T over 64 keys ----
-    floatx16 st[2];
+  // S^T = K Q^T for the 64 keys of a K buffer.
+  auto qk = [&](const uint8_t* kbuf, floatx16 (&st)[2]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[t][e] = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + koff[kc] + 32 * t * C::ROWB);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + koff[kc] + 32 * t * C::ROWB);
         st[t] = mfma32x32x16(as_bf16x8(a), qb[kc], st[t]);
       }
     }
+  };
 
-    // ---- causal mask on the diagonal block, row max ----
-    if (J == I) {
+  // Pipeline over sub-tiles t = 0 .. n_sub-1 (block J(t) = block_of(t)).  K runs
+  // one sub-tile ahead of V: iteration s computes S(s+1) = K(s+1) Q^T with the
+  // MFMA unit while the VALU turns S(s) into probabilities, then O += V(s) P(s).
+  // Copies issued in iteration s: V(s+1) and K(s+2), into the buffers that held
+  // V(s-1) and K(s), both consumed before the previous closing barrier.
+  floatx16 st_cur[2];
+  int J_cur = 0, J_n1 = 0;
+  if (n_sub > 0) {
+    J_cur = block_of(0);
+    copy_tile(kbase, 0, J_cur, kb0);
+    copy_tile(vbase, 0, J_cur, vb0);
+    if (n_sub > 1) {
+      J_n1 = block_of(1);
+      copy_tile(kbase, 1, J_n1, kb1);
+      wait_vmcnt<2 * C::IPW>();
+    } else {
+      wait_vmcnt<C::IPW>();
+    }
+    lds_barrier();  // K(0) landed for every wave
+    qk(kb0, st_cur);
+  }
+
+  auto step = [&](int s, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
+    // kcur = K(s+1), vcur = V(s); V(s+1) -> vnext, K(s+2) -> knext.
+    int J_n2 = J_n1;
+    if (s + 2 < n_sub) {
+      J_n2 = block_of(s + 2);
+      copy_tile(vbase, s + 1, J_n1, vnext);
+      copy_tile(kbase, s + 2, J_n2, knext);
+      wait_vmcnt<2 * C::IPW>();
+    } else if (s + 1 < n_sub) {
+      copy_tile(vbase, s + 1, J_n1, vnext);
+      wait_vmcnt<C::IPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // V(s) and K(s+1) landed for every wave
+
+    // Causal mask of S(s) when it lies in the diagonal block (rare; own branch).
+    if (J_cur == I) {
+      const int key_base = (s % C::SUB) * C::KT;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key_local = key_base + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key_local > q_local) st[t][e] = -INFINITY;
+          if (key_local > q_local) st_cur[t][e] = -INFINITY;
         }
     }
+
+    // ---- S(s+1) on the MFMA unit, softmax of S(s) on the VALU ----
+    // Row max of S(s) first (it gates every exponential).
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[t][e]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 32)) * c;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st_cur[t][e]);
+    mx = max_halves(mx) * c;
     const bool raise = mx > m;  // m = -inf on the first sub-tile
+    const float m_new = raise ? mx : m;
+    // 16 chunks, each one MFMA of S(s+1) = K(s+1) Q^T (MFMA i: key tile i / KC,
+    // k-chunk i % KC), one probability pair of S(s), and the LDS read of the
+    // K fragment four MFMAs ahead; sched_barrier keeps the chunks in order so
+    // the MFMA unit and the VALU work side by side.  (For the last sub-tile the
+    // product re-reads a stale K buffer; its result is unused.)
+    floatx16 st_next[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st_next[t][e] = 0.0f;
+    constexpr int NM = 2 * C::KC;  // MFMAs of one 64-key S^T tile
+    constexpr int AHEAD = 4;
+    u32x4 kf[NM];
+    auto kfrag = [&](int i) {
+      return *reinterpret_cast<const u32x4*>(kcur + koff[i % C::KC] + 32 * (i / C::KC) * C::ROWB);
+    };
+#pragma unroll
+    for (int i = 0; i < AHEAD; ++i) kf[i] = kfrag(i);
+    u32x4 pb[2][2];
+    float lsum = 0.0f;
+    constexpr int NCHUNK = NM > 16 ? NM : 16;  // 16 probability pairs per sub-tile
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      if (i + AHEAD < NM) kf[i + AHEAD] = kfrag(i + AHEAD);
+      if (i < NM) st_next[i / C::KC] = mfma32x32x16(as_bf16x8(kf[i]), qb[i % C::KC], st_next[i / C::KC]);
+      if (i < 16) {
+        const int t = i >> 3, u = (i >> 2) & 1, e = i & 3;
+        const float p0 = fast_exp2(fmaf(st_cur[t][8 * u + 2 * e], c, -m_new));
+        const float p1 = fast_exp2(fmaf(st_cur[t][8 * u + 2 * e + 1], c, -m_new));
+        pb[t][u][e] = pack_bf16x2(p0, p1);
+        lsum = add_bf16x2(pb[t][u][e], lsum);  // the same rounded p as V^T P^T
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Keep the probabilities in this block (ahead of the rescale branch).
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) asm volatile("" ::"v"(pb[t][u]));
+    asm volatile("" ::"v"(lsum));
+
     if (__any(raise)) {
-      const float m_new = raise ? mx : m;
       const float alpha = fast_exp2(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int ct = 0; ct < C::CT; ++ct)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
-      m = m_new;
     }
+    m = m_new;
+    l += lsum;
 
-    // ---- probabilities (bf16, B operand of the second product) ----
-    u32x4 pb[2][2];
+    // ---- O^T += V^T P^T: 16 MFMAs, V^T fragments read AV MFMAs ahead ----
+    constexpr int NP = 4 * C::CT;  // (t, u, ct) triples
+    constexpr int AV = 3;
+    u32x4 vf[NP];
+    auto vfrag = [&](int j) {
+      const int t = j / (2 * C::CT), u = (j / C::CT) & 1, ct = j % C::CT;
+      const int rowoff = (32 * t + 16 * u) * C::ROWB;
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(vcur + rowoff + voff[0][ct]));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(vcur + rowoff + voff[1][ct]));
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+      return a;
+    };
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int j = 0; j < AV; ++j) vf[j] = vfrag(j);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+    for (int j = 0; j < NP; ++j) {
+      if (j + AV < NP) vf[j + AV] = vfrag(j + AV);
+      const int t = j / (2 * C::CT), u = (j / C::CT) & 1, ct = j % C::CT;
+      o[ct] = mfma32x32x16(as_bf16x8(vf[j]), as_bf16x8(pb[t][u]), o[ct]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lds_reads_done_barrier();  // every wave is done with K(s+1)'s and V(s)'s buffers
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(st[t][8 * u + 2 * e], c, -m));
-          const float p1 = fast_exp2(fmaf(st[t][8 * u + 2 * e + 1], c, -m));
-          pb[t][u][e] = pack_bf16x2(p0, p1);
-          l = add_bf16x2(pb[t][u][e], l);  // the denominator sums the same rounded p as V^T P^T
-        }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int rowoff = (32 * t + 16 * u) * C::ROWB;
-#pragma unroll
-        for (int ct = 0; ct < C::CT; ++ct) {
-          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4_t*)(Vs + rowoff + voff[0][ct]));
-          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) short4_t*)(Vs + rowoff + voff[1][ct]));
-          u32x4 a;
-          a[0] = static_cast<uint16_t>(lo[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16);
-          a[1] = static_cast<uint16_t>(lo[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16);
-          a[2] = static_cast<uint16_t>(hi[0]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16);
-          a[3] = static_cast<uint16_t>(hi[2]) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16);
-          o[ct] = mfma32x32x16(as_bf16x8(a), as_bf16x8(pb[t][u]), o[ct]);
-        }
-      }
-    lds_reads_done_barrier();  // every wave is done with this stage before it is refilled
-    J = J_next;
+    for (int t = 0; t < 2; ++t) st_cur[t] = st_next[t];
+    J_cur = J_n1;
+    J_n1 = J_n2;
   };
   for (int s = 0; s < n_sub; s += 2) {
-    step(s, stage0, stage1);
-    if (s + 1 < n_sub) step(s + 1, stage1, stage0);
+    step(s, kb1, vb0, kb0, vb1);
+    if (s + 1 < n_sub) step(s + 1, kb0, vb1, kb1, vb0);
   }
 
   // ---- normalise and store: lane holds 4 consecutive channels per group ----
-  l += shfl_xor_f(l, 32);
+  l = sum_halves(l);
   const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
   uint16_t* orow = out + ((static_cast<int64_t>(b) * H + h) * L + q_tok) * D;
 #pragma unroll
