@@ -17,7 +17,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -31,7 +30,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=1, n_rows_sample=4):
+def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=4, n_rows_sample=16):
     """The fp64 CPU oracle on a bounded sample of the same workload.
 
     Times the oracle's estimator on n_heads_sample query heads (full length)
@@ -61,7 +60,6 @@ def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=1, n_rows_sa
     t_est = (time.perf_counter() - t0) / n_heads_sample * w.num_heads * w.batch
     rng = np.random.default_rng(0)
     rows = [(0, int(rng.integers(0, w.num_heads)), int(rng.integers(nb // 2, nb))) for _ in range(n_rows_sample)]
-    qn = {}
     t_attn_sample = 0.0
     blocks_sample = 0
     for (b, h, i) in rows:
@@ -75,7 +73,6 @@ def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=1, n_rows_sa
         orc.attention_rows(sub_q, sub_k, sub_v, mrow, one, 0, 0, i)
         t_attn_sample += time.perf_counter() - t1
         blocks_sample += int(cnt[b, h, i])
-        qn[(b, h, i)] = True
     t_attn = t_attn_sample / max(blocks_sample, 1) * float(cnt.sum())
     t_total = t_est + t_attn
     return {
