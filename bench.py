@@ -96,9 +96,12 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "profile", "power"], default="bench",
                     help="profile: one estimate, --steps sparse-attention launches, one dense launch and a "
-                         "256 MiB device copy (HBM-counter calibration); prints a short summary only")
+                         "256 MiB device copy (HBM-counter calibration); prints a short summary only. "
+                         "power: socket power (amd-smi) while sparse attention, dense attention and the "
+                         "MFMA probe each run back to back for --power-secs seconds")
+    ap.add_argument("--power-secs", type=float, default=6.0)
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic_sparse_attn_llama_128k.json"))
     args = ap.parse_args(argv)
@@ -149,6 +152,16 @@ def main(argv=None) -> int:
         dst.copy_(src)  # calibration: reads and writes exactly COPY_BYTES
         torch.cuda.synchronize()
         log(f"[bench] profile run done: sum(cnt) = {int(sel.cnt.sum())}, copy {COPY_BYTES} B")
+        return 0
+
+    if args.mode == "power":
+        rra.estimate(p, qd, kd, workspace=ws, out=sel)
+        torch.cuda.synchronize()
+        f_sel = 4.0 * w.head_dim * w.block * w.block * int(sel.cnt.sum())
+        f_full = 4.0 * w.head_dim * w.block * w.block * p.batch * p.num_heads * nb * (nb + 1) // 2
+        print(json.dumps(power_report(
+            lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out), f_sel,
+            lambda: rra.dense_attn(p, qd, kd, vd, out=dense_out), f_full, args.power_secs)), flush=True)
         return 0
 
     log(f"[bench] warmup {args.warmup}")
@@ -261,6 +274,10 @@ def main(argv=None) -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": f_sel, "avg_launch_ms": round(t_sp, 4)},
     }
+    ceil = mfma_ceiling()
+    if ceil is not None:
+        ceil["sparse_attn_frac_of_random_operand_rate"] = round(achieved / ceil["random_operands"]["tflops"], 4)
+    line["mfma_sustained"] = ceil
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline (bounded sample)")
         cb = cpu_baseline(q, k, v, sel.mask.cpu().numpy(), cnt.numpy(), w, f_dense)
@@ -269,6 +286,115 @@ def main(argv=None) -> int:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
     return 0
+
+
+def mfma_ceiling() -> dict | None:
+    """Sustained bf16 MFMA rate and shader clock of a pure matrix-core loop
+    (librra_probe.so), with zero and with random N(0,1) operands."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd",
+                        "librra_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.rra_probe_mfma_rate
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    res = {}
+    for name, operands in (("zero_operands", 0), ("random_operands", 1)):
+        # ~0.5 s of warm-up lets the clock settle after the attention runs (the
+        # power manager reacts over tens of ms); then the median of 3 runs of ~60 ms
+        runs = []
+        t0 = time.time()
+        while True:
+            tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
+            rc = fn(operands, 200000, ctypes.byref(tf), ctypes.byref(ghz))
+            if rc != 0:
+                log(f"[bench] MFMA probe failed with HIP error {rc}")
+                return None
+            if time.time() - t0 > 0.5:
+                runs.append((tf.value, ghz.value))
+            if len(runs) == 3:
+                break
+        runs.sort()
+        res[name] = {"tflops": round(runs[1][0], 1), "clock_ghz": round(runs[1][1], 3)}
+    return res
+
+
+def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
+    """Median socket power (amd-smi, sampled from a thread) while each workload
+    runs back to back, its rate, and the energy per flop above idle."""
+    import ctypes
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run(["amd-smi", "metric", "--power"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+                if m:
+                    samples.append((time.time(), float(m.group(1))))
+            except Exception:
+                pass
+            time.sleep(0.1)
+
+    probe_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd",
+                              "librra_probe.so")
+    probe = ctypes.CDLL(probe_path).rra_probe_mfma_rate
+    probe.restype = ctypes.c_int
+    probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    last = {}
+
+    def mfma(operands):
+        tf, ghz = ctypes.c_double(), ctypes.c_double()
+        assert probe(operands, 200000, ctypes.byref(tf), ctypes.byref(ghz)) == 0
+        last["tflops"], last["clock_ghz"] = tf.value, ghz.value
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    phases = []
+    time.sleep(2.0)
+    phases.append(("idle", time.time() - 2.0, time.time(), None, None))
+    for name, fn, flops in (("sparse_attn", sparse_fn, f_sparse), ("dense_attn", dense_fn, f_dense),
+                            ("mfma_probe_random_operands", lambda: mfma(1), None),
+                            ("mfma_probe_zero_operands", lambda: mfma(0), None)):
+        fn()
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        while time.time() - t0 < secs:
+            fn()
+            torch.cuda.synchronize()
+            n += 1
+        t1 = time.time()
+        rate = flops * n / (t1 - t0) / 1e12 if flops else last["tflops"]
+        phases.append((name, t0, t1, rate, None if flops else last["clock_ghz"]))
+        log(f"[bench] power phase {name}: {n} runs")
+        time.sleep(1.5)
+    stop.set()
+    th.join(timeout=15)
+    res = {"mode": "power", "samples": len(samples), "phases": {}}
+    idle_w = None
+    for name, t0, t1, rate, ghz in phases:
+        v = sorted(wt for ts, wt in samples if t0 + 0.8 < ts < t1 - 0.2)
+        med = v[len(v) // 2] if v else None
+        if name == "idle":
+            idle_w = med
+        entry = {"median_w": med, "n_samples": len(v)}
+        if rate is not None:
+            entry["tflops"] = round(rate, 1)
+            if med is not None and idle_w is not None:
+                entry["pj_per_flop_above_idle"] = round((med - idle_w) / (rate * 1e12) * 1e12, 3)
+        if ghz is not None:
+            entry["clock_ghz"] = round(ghz, 3)
+        res["phases"][name] = entry
+    return res
 
 
 def _kernel_hash() -> str:

@@ -138,8 +138,12 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   // ---- work item ----
   // Workgroup w runs on XCD w mod 8.  The KV groups are processed in phases of
   // `gp` groups (their K and V fit the memory-side cache together); inside a
-  // phase XCD x takes group x mod gp and every (8/gp)-th query block, longest
-  // rows first, the heads of a group next to each other.
+  // phase XCD x takes every (8/gp)-th query block, longest rows first, the
+  // heads of a group next to each other (they stream the same K/V through the
+  // XCD's L2).  The group an XCD serves rotates every 16 slots (about the
+  // workgroups an XCD holds at once, so neighbouring query blocks of a group,
+  // whose lists overlap, still share the L2): groups differ in density, and a
+  // fixed assignment would leave the XCDs of the sparser groups idle at the end.
   const int nbg = static_cast<int>(gridDim.x / (static_cast<unsigned>(G) * Nb));  // Bz * Hkv
   int bg, hh, I;
   {
@@ -154,7 +158,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
       hh = slot % G;
       slot /= G;
       I = Nb - 1 - (slot * split + xcd / gp);
-      bg = ph * gp + xcd % gp;
+      bg = ph * gp + (xcd + (slot >> 4)) % gp;
     } else {
       int t = w;
       hh = t % G;

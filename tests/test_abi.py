@@ -33,6 +33,19 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert set(_lib.SIGNATURES) == set(names)
 
 
+def test_probe_library_exports_its_header():
+    """librra_probe.so (the bench's sustained-MFMA-rate probe) exports what rra_probe.h declares."""
+    path = os.path.join(os.path.dirname(_lib.LIB_PATH), "librra_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("librra_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rra_probe.h")).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+(rra_\w+)\s*\(", text, flags=re.M)
+    assert names == ["rra_probe_mfma_rate"]
+    lib = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
 def test_params_struct_matches_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct rra_params \{(.*?)\} rra_params_t;", text, flags=re.S).group(1)
