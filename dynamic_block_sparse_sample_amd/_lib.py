@@ -41,6 +41,9 @@ class Params(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("protect_last", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
+        ("rr_mode", ctypes.c_int32),
+        ("rr_layer", ctypes.c_int32),
+        ("rr_offset", ctypes.c_int32),
     ]
 
     def __repr__(self):
@@ -103,10 +106,17 @@ def _check(fn: str, code: int) -> None:
         raise RRAError(fn, code)
 
 
+# Round-robin strategies (rra_rr_mode_t): offset of the sampled query inside a stride.
+RR_MODES = {"head": 0, "layer": 1, "hybrid": 2, "none": 3}
+
+
 def make_params(batch, num_heads, num_kv_heads, seq_len, head_dim, stride, block, tau,
-                protect_last=True, sm_scale=0.0, causal=True) -> Params:
+                protect_last=True, sm_scale=0.0, causal=True, rr_mode="head", rr_layer=0,
+                rr_offset=0) -> Params:
     return Params(int(batch), int(num_heads), int(num_kv_heads), int(seq_len), int(head_dim), int(stride),
-                  int(block), float(tau), int(bool(causal)), int(bool(protect_last)), float(sm_scale))
+                  int(block), float(tau), int(bool(causal)), int(bool(protect_last)), float(sm_scale),
+                  RR_MODES[rr_mode] if isinstance(rr_mode, str) else int(rr_mode), int(rr_layer),
+                  int(rr_offset))
 
 
 def validate(p: Params) -> int:

@@ -4,7 +4,9 @@
 //
 // One wave per (batch, KV group g, query block I, row tile).  A row tile holds
 // 32 sampled queries: strides i of block I for the G query heads of group g,
-// taken at positions P(i,h) = i*S + (h mod S).  The wave computes the
+// taken at positions P(i,h) = i*S + o(h), o(h) = (rr_step * h + rr_shift) mod S
+// (head round-robin: h mod S; the layer / hybrid / fixed variants of the
+// §4.3 ablation change only o).  The wave computes the
 // transposed score tile S^T = Kagg_tile x Q_sampled^T with
 // v_mfma_f32_32x32x16_bf16 (A = 32 aggregated keys, B = 32 sampled queries),
 // so every lane owns one sampled query (lane & 31) and 16 of the 32 strides of
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ kagg,
                                                           float* __restrict__ score, int H, int Hkv,
                                                           int G, int L, int S, int Ns, int Nb, int n_rt,
-                                                          int nbg, float c) {
+                                                          int nbg, float c, int rr_step, int rr_shift) {
   constexpr int KC = D / 16;
   const int lane = threadIdx.x;
   const int col = lane & 31;
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
   const int ii = rho % R;
   const int h = g * G + hh;
   const int i = I * R + ii;         // sampled stride
-  const int64_t pos = static_cast<int64_t>(i) * S + (h % S);
+  const int64_t pos = static_cast<int64_t>(i) * S + (rr_step * h + rr_shift) % S;
 
   bf16x8 qb[KC];
   {
@@ -202,7 +204,8 @@ static void launch_bs(const Shape& s, const uint16_t* q, const uint16_t* kagg, f
   const int64_t blocks = static_cast<int64_t>(n_rt) * nbg * s.Nb;
   const float c = s.scale * kLog2e;
   hipLaunchKernelGGL((block_scores_kernel<D, R>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, st, q, kagg,
-                     score, s.H, s.Hkv, s.G, s.L, s.S, s.Ns, s.Nb, n_rt, nbg, c);
+                     score, s.H, s.Hkv, s.G, s.L, s.S, s.Ns, s.Nb, n_rt, nbg, c, s.rr_step,
+                     s.rr_shift);
 }
 
 template <int D>

@@ -19,6 +19,9 @@ struct Shape {
   int Nb;  // L / Bk
   int r;   // Bk / S, strides per block
   float scale;
+  // Sampled offset inside a stride for query head h: (rr_step * h + rr_shift) mod S.
+  int rr_step;   // 1 for head / hybrid round-robin, 0 otherwise
+  int rr_shift;  // in [0, S)
 };
 
 Shape shape_of(const rra_params_t& p);

@@ -22,6 +22,13 @@ Shape shape_of(const rra_params_t& p) {
   s.Nb = p.seq_len / (p.block > 0 ? p.block : 1);
   s.r = p.block / (p.stride > 0 ? p.stride : 1);
   s.scale = (p.sm_scale > 0.0f) ? p.sm_scale : 1.0f / std::sqrt(static_cast<float>(p.head_dim));
+  const int S = p.stride > 0 ? p.stride : 1;
+  switch (p.rr_mode) {
+    case RRA_RR_LAYER: s.rr_step = 0; s.rr_shift = p.rr_layer % S; break;
+    case RRA_RR_HYBRID: s.rr_step = 1; s.rr_shift = p.rr_layer % S; break;
+    case RRA_RR_NONE: s.rr_step = 0; s.rr_shift = p.rr_offset; break;
+    default: s.rr_step = 1; s.rr_shift = 0; break;  // RRA_RR_HEAD
+  }
   return s;
 }
 
@@ -64,6 +71,8 @@ rra_status_t rra_validate(const rra_params_t* p) {
   if (p->protect_last != 0 && p->protect_last != 1) return RRA_ERR_INVALID_ARG;
   if (p->causal != 0 && p->causal != 1) return RRA_ERR_INVALID_ARG;
   if (p->block % p->stride != 0) return RRA_ERR_INVALID_ARG;  // a block holds whole strides
+  if (p->rr_mode < RRA_RR_HEAD || p->rr_mode > RRA_RR_NONE) return RRA_ERR_INVALID_ARG;
+  if (p->rr_layer < 0 || p->rr_offset < 0 || p->rr_offset >= p->stride) return RRA_ERR_INVALID_ARG;
   // Shapes the kernels are built for.
   if (p->causal != 1) return RRA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return RRA_ERR_UNSUPPORTED;

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 1
+#define RRA_ABI_VERSION 2
 
 typedef enum rra_status {
   RRA_OK = 0,
@@ -50,11 +50,28 @@ typedef enum rra_status {
   RRA_ERR_HIP = 4          /* the HIP runtime reported an error            */
 } rra_status_t;
 
+/* Round-robin strategies (§4.3 Round-Robin Strategy ablation: head-RR,
+ * layer-RR, hybrid-RR and no RR; the page names them without formulas).
+ * The offset o(h) of the sampled query inside every stride, for query head h
+ * of layer l = rr_layer, is read as:
+ *   RRA_RR_HEAD    o = h mod S              (the method's default, §3.1)
+ *   RRA_RR_LAYER   o = l mod S              (same for every head of a layer)
+ *   RRA_RR_HYBRID  o = (h + l) mod S
+ *   RRA_RR_NONE    o = rr_offset            (fixed, 0 <= rr_offset < S)     */
+typedef enum rra_rr_mode {
+  RRA_RR_HEAD = 0,
+  RRA_RR_LAYER = 1,
+  RRA_RR_HYBRID = 2,
+  RRA_RR_NONE = 3
+} rra_rr_mode_t;
+
 /* Problem description (§2.1: Q, K of one head are L x d, split into blocks
  * of Bk tokens, with a finer sampling stride S; §3.3: threshold tau;
  * causal prefill, §4.1).  Supported: H % Hkv == 0; d in {64, 128};
  * Bk in {64, 128}; L % Bk == 0; Bk % S == 0 and Bk / S <= 32;
- * L / Bk <= 4096; 0 < tau <= 1; causal == 1; protect_last in {0, 1}.
+ * L / Bk <= 4096; 0 < tau <= 1; causal == 1; protect_last in {0, 1};
+ * rr_mode in rra_rr_mode_t; rr_layer >= 0; 0 <= rr_offset < S.
+ * A zero-filled tail (rr_mode = rr_layer = rr_offset = 0) is head-RR.
  * batch == 0 or seq_len == 0 is a valid empty problem: every entry point
  * returns RRA_OK without touching memory. */
 typedef struct rra_params {
@@ -70,6 +87,9 @@ typedef struct rra_params {
   int32_t protect_last; /* 1: the last query-block row keeps every causal
                            key block (§4.3, last query block protection)  */
   float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim)      */
+  int32_t rr_mode;      /* rra_rr_mode_t, 0 = head round-robin             */
+  int32_t rr_layer;     /* layer index l for RRA_RR_LAYER / RRA_RR_HYBRID  */
+  int32_t rr_offset;    /* fixed offset for RRA_RR_NONE                    */
 } rra_params_t;
 
 /* RRA_ABI_VERSION of the loaded library. */
@@ -95,7 +115,8 @@ rra_status_t rra_stride_aggregate(const rra_params_t* p, const void* k, void* ka
 
 /* Round-robin sampled stride scores, stride softmax and block pooling
  * (§3.1, §3.2, §2.2 query independence).  For query head h the query of
- * stride i is taken at position P(i,h) = i*S + (h mod S); its scores
+ * stride i is taken at position P(i,h) = i*S + o(h), o(h) = h mod S for
+ * head-RR (other strategies: rra_rr_mode_t); its scores
  * s[i,j] = sm_scale * <q[P(i,h)], kagg[j]> over strides j <= i are softmax
  * normalised per sampled query, and pooled:
  *   score[b,h,I,J] = (1/r) * sum_{i in block I} sum_{j in block J, j <= i} p[i,j],

@@ -24,6 +24,9 @@ formula of §3.1, the score equation of §3.2, all of §3.3).  The readings used
 here are:
 
   * sampled position  P(i, h) = i*S + (h mod S)                    (§3.1, §7)
+  * round-robin variants of the §4.3 ablation (named there, not defined):
+                      layer-RR  o = l mod S, hybrid-RR  o = (h + l) mod S,
+                      no RR  o = a fixed offset c, with P(i, h) = i*S + o
   * aggregated key    Kagg[j] = bf16_rne( (sum of K over stride j) / S )
                       -- the 1/S of the §3.2 normalisation folded into the
                       stride mean; the bf16 rounding is part of the library's
@@ -56,6 +59,7 @@ import numpy as np
 __all__ = [
     "Params",
     "bf16_round",
+    "rr_offset",
     "rr_positions",
     "aggregate_keys",
     "stride_scores",
@@ -85,6 +89,9 @@ class Params:
     tau: float
     protect_last: bool = True
     sm_scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
+    rr_mode: str = "head"  # "head", "layer", "hybrid" or "none" (§4.3 ablation)
+    rr_layer: int = 0  # layer index l for "layer" and "hybrid"
+    rr_fixed: int = 0  # the offset for "none"
 
     @property
     def scale(self) -> float:
@@ -136,14 +143,36 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # §3.1: head round-robin query sampling.
 # ---------------------------------------------------------------------------
-def rr_positions(num_strides: int, stride: int, head: int) -> np.ndarray:
+def rr_offset(head: int, stride: int, mode: str = "head", layer: int = 0, fixed: int = 0) -> int:
+    """Offset inside every stride of the query sampled for `head`.
+
+    head-RR (the method, §3.1): the offset rotates with the head index.  The
+    §4.3 ablation also names layer-RR, hybrid-RR and no RR without formulas;
+    read as rotating with the layer index, with head plus layer, and not at
+    all (one fixed offset for every head and layer).
+    """
+    if mode == "head":
+        return head % stride
+    if mode == "layer":
+        return layer % stride
+    if mode == "hybrid":
+        return (head + layer) % stride
+    if mode == "none":
+        if not 0 <= fixed < stride:
+            raise ValueError("fixed offset outside the stride")
+        return fixed
+    raise ValueError(f"unknown round-robin mode {mode!r}")
+
+
+def rr_positions(num_strides: int, stride: int, head: int, mode: str = "head", layer: int = 0,
+                 fixed: int = 0) -> np.ndarray:
     """Token position sampled from each stride i for query head `head`.
 
     One query per stride of S tokens; the offset inside the stride rotates
     with the head index (RRAttention §1, §3.1 and the abstract) and does not
     depend on i, so with S > H some offsets are never sampled (§7).
     """
-    return np.arange(num_strides, dtype=np.int64) * stride + (head % stride)
+    return np.arange(num_strides, dtype=np.int64) * stride + rr_offset(head, stride, mode, layer, fixed)
 
 
 # ---------------------------------------------------------------------------
@@ -167,7 +196,7 @@ def aggregate_keys(k_head: np.ndarray, stride: int, kagg_round: str = "bf16") ->
 
 
 def stride_scores(q_head: np.ndarray, kagg: np.ndarray, stride: int, head: int,
-                  sm_scale: float) -> np.ndarray:
+                  sm_scale: float, mode: str = "head", layer: int = 0, fixed: int = 0) -> np.ndarray:
     """s[i, j] = sm_scale * <Q[P(i, h)], Kagg[j]> for j <= i, -inf above.
 
     With Kagg the stride mean, sm_scale = 1/sqrt(d) gives the page's
@@ -175,7 +204,7 @@ def stride_scores(q_head: np.ndarray, kagg: np.ndarray, stride: int, head: int,
     Every stride j <= i is visible, the diagonal stride included.
     """
     ns = kagg.shape[0]
-    qs = q_head[rr_positions(ns, stride, head)]  # [Ns, d]
+    qs = q_head[rr_positions(ns, stride, head, mode, layer, fixed)]  # [Ns, d]
     s = sm_scale * (qs @ kagg.T)
     s[np.triu_indices(ns, k=1)] = -np.inf
     return s
@@ -207,7 +236,8 @@ def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "b
             kagg = aggregate_keys(k[b, g], prm.stride, kagg_round)
             for hh in range(prm.group):
                 h = g * prm.group + hh
-                s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale)
+                s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale, prm.rr_mode, prm.rr_layer,
+                                  prm.rr_fixed)
                 out[b, h] = pool_blocks(stride_softmax(s), prm.strides_per_block)
     return out
 

@@ -28,11 +28,13 @@ def out_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref) - half_ulp))
 
 
-def oracle_params(w, tau=None, stride=None, protect_last=True) -> orc.Params:
+def oracle_params(w, tau=None, stride=None, protect_last=True, rr_mode="head", rr_layer=0,
+                  rr_fixed=0) -> orc.Params:
     t = w.tau if tau is None else tau
     return orc.Params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim,
                       w.stride if stride is None else stride, w.block,
-                      float(np.float32(t)), protect_last)
+                      float(np.float32(t)), protect_last, rr_mode=rr_mode, rr_layer=rr_layer,
+                      rr_fixed=rr_fixed)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

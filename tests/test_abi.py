@@ -54,11 +54,11 @@ def test_params_struct_matches_header():
     assert [f for _, f in fields] == [n for n, _ in rra.Params._fields_]
     for (ty, _), (_, cty) in zip(fields, rra.Params._fields_):
         assert cty == (ctypes.c_int32 if ty == "int32_t" else ctypes.c_float)
-    assert ctypes.sizeof(rra.Params) == 44
+    assert ctypes.sizeof(rra.Params) == 56
 
 
 def test_abi_version_and_status_strings():
-    assert rra.lib().rra_abi_version() == 1
+    assert rra.lib().rra_abi_version() == 2
     for code in range(5):
         assert rra.status_str(code).startswith("RRA_")
     assert rra.status_str(99) == "RRA_ERR_UNKNOWN"
@@ -95,6 +95,14 @@ def P(**kw):
     (dict(stride=2), 2),  # Bk / S = 64 > 32
     (dict(causal=False), 2),
     (dict(seq_len=128 * 4097), 2),  # more than 4096 blocks
+    (dict(rr_mode="layer", rr_layer=31), 0),
+    (dict(rr_mode="hybrid", rr_layer=7), 0),
+    (dict(rr_mode="none", rr_offset=15), 0),
+    (dict(rr_mode=4), 1),
+    (dict(rr_mode=-1), 1),
+    (dict(rr_layer=-1), 1),
+    (dict(rr_mode="none", rr_offset=16), 1),  # offset must lie inside the stride
+    (dict(rr_offset=-1), 1),
 ])
 def test_validate_status_codes(kw, code):
     assert rra.validate(P(**kw)) == code

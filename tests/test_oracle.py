@@ -94,6 +94,65 @@ def test_rr_positions_hand_worked_table():
 # ---------------------------------------------------------------------------
 # stride aggregation
 # ---------------------------------------------------------------------------
+def test_rr_variant_offsets_hand_worked_table():
+    rows = [ln for ln in open(os.path.join(GOLDEN, "rr_variants.txt")) if ln.strip() and not ln.startswith("#")]
+    assert len(rows) == 13
+    for ln in rows:
+        head, offs = ln.split("|")
+        mode, H, S, layer, fixed = head.split()
+        H, S, layer, fixed = int(H), int(S), int(layer), int(fixed)
+        want = [int(x) for x in offs.split()]
+        assert [orc.rr_offset(h, S, mode, layer, fixed) for h in range(H)] == want, ln
+        # the offset is the same in every stride
+        for h in range(H):
+            pos = orc.rr_positions(5, S, h, mode, layer, fixed)
+            assert (pos - np.arange(5) * S).tolist() == [want[h]] * 5
+
+
+def test_rr_variant_coverage_over_layers():
+    """Over S consecutive layers, layer-RR and hybrid-RR sample every offset
+    exactly once per head; head-RR and no RR never move."""
+    S, H = 8, 4
+    for mode in ("layer", "hybrid"):
+        for h in range(H):
+            offs = sorted(orc.rr_offset(h, S, mode, l0) for l0 in range(3, 3 + S))
+            assert offs == list(range(S))
+    for h in range(H):
+        assert len({orc.rr_offset(h, S, "head", l0) for l0 in range(S)}) == 1
+        assert {orc.rr_offset(h, S, "none", l0, 5) for l0 in range(S)} == {5}
+    with pytest.raises(ValueError):
+        orc.rr_offset(0, S, "none", 0, S)
+    with pytest.raises(ValueError):
+        orc.rr_offset(0, S, "diagonal", 0, 0)
+
+
+def test_rr_variants_reach_the_block_scores():
+    """hybrid-RR of head h at layer l samples Q[h] where head-RR samples head
+    (h + l) mod S: with one KV head and H = S, moving Q[h] to head (h + l) mod S
+    turns one result into the other (equivariance, so the mode is wired
+    through stride_scores and block_scores, not only rr_positions)."""
+    S, H, L, d, Bk, layer = 4, 4, 64, 16, 16, 3
+    rng = np.random.default_rng(7)
+    q = orc.bf16_round(rng.standard_normal((1, H, L, d)))
+    k = orc.bf16_round(rng.standard_normal((1, 1, L, d)))
+    hyb = orc.Params(1, H, 1, L, d, S, Bk, 0.9, rr_mode="hybrid", rr_layer=layer)
+    hd = orc.Params(1, H, 1, L, d, S, Bk, 0.9)
+    q_perm = np.empty_like(q)
+    for h in range(H):
+        q_perm[0, (h + layer) % S] = q[0, h]
+    m_hyb = orc.block_scores(q, k, hyb)
+    m_head = orc.block_scores(q_perm, k, hd)
+    for h in range(H):
+        assert np.array_equal(m_hyb[0, h], m_head[0, (h + layer) % S])
+    # and the modes really differ: layer-RR gives every head the same offset
+    lay = orc.Params(1, H, 1, L, d, S, Bk, 0.9, rr_mode="layer", rr_layer=layer)
+    m_lay = orc.block_scores(q, k, lay)
+    assert not np.array_equal(m_lay, m_head)
+    q_same = np.repeat(q[:, :1], H, axis=1)
+    m_same = orc.block_scores(q_same, k, lay)
+    assert all(np.array_equal(m_same[0, 0], m_same[0, h]) for h in range(H))
+
+
 def test_aggregate_constant_stride_is_that_constant():
     rng = np.random.default_rng(2)
     per_stride = _bf16_values((16, 8), rng)

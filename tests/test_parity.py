@@ -127,6 +127,40 @@ def test_small_cases_all_steps(case):
     assert err <= OUT_ATOL
 
 
+RR_CASES = [("layer", 5, 0), ("hybrid", 11, 0), ("none", 0, 3), ("none", 0, -1), ("head", 9, 0)]
+
+
+@pytest.mark.parametrize("shape", [SMALL[0], SMALL[5], SMALL[8]], ids=[SMALL[0][0], SMALL[5][0], SMALL[8][0]])
+@pytest.mark.parametrize("rr", RR_CASES, ids=[f"{m}_l{l0}_c{c}" for m, l0, c in RR_CASES])
+def test_round_robin_variants(shape, rr):
+    """§4.3 round-robin strategies: block scores and masks against the oracle
+    (offset -1 stands for S - 1, the last position of every stride)."""
+    mode, layer, fixed = rr
+    name, B, H, Hkv, L, d, S, Bk, tau = shape
+    fixed = S - 1 if fixed < 0 else fixed
+    q, k, _ = wl.make_random(B, H, Hkv, L, d, seed=4, scale=1.5, diag=1.0)
+    prm = orc.Params(B, H, Hkv, L, d, S, Bk, float(np.float32(tau)), True, rr_mode=mode, rr_layer=layer,
+                     rr_fixed=fixed)
+    p = rra.make_params(B, H, Hkv, L, d, S, Bk, tau, rr_mode=mode, rr_layer=layer, rr_offset=fixed)
+    say("rr case", name, mode, layer, fixed)
+    qd, kd = q.cuda(), k.cuda()
+    sel = rra.estimate(p, qd, kd, return_score=True)
+    torch.cuda.synchronize()
+    m_or = orc.block_scores(to_f64(q), to_f64(k), prm)
+    err = float(np.max(np.abs(to_f64(sel.score) - m_or)))
+    assert err <= SCORE_ATOL, err
+    checked, near, bad = compare_masks(sel.mask.cpu().numpy(), sel.cnt.cpu().numpy(), sel.idx.cpu().numpy(),
+                                       m_or, prm)
+    say(f"  score err {err:.1e}, mask rows {checked}, near-tie rows {near}")
+    assert not bad, bad[:5]
+    # the strategy matters: head-RR scores differ unless the offsets coincide
+    p_head = rra.make_params(B, H, Hkv, L, d, S, Bk, tau)
+    sel_head = rra.estimate(p_head, qd, kd, return_score=True)
+    torch.cuda.synchronize()
+    same_offsets = all(orc.rr_offset(h, S, mode, layer, fixed) == h % S for h in range(H))
+    assert torch.equal(sel.score, sel_head.score) == same_offsets
+
+
 def test_tiny_workload_end_to_end():
     w = wl.WORKLOADS["tiny_1k"]
     q32, k32, v32 = wl.make_inputs(w)
