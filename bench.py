@@ -96,11 +96,14 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile", "power"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "profile", "power", "selection"], default="bench",
                     help="profile: one estimate, --steps sparse-attention launches, one dense launch and a "
                          "256 MiB device copy (HBM-counter calibration); prints a short summary only. "
                          "power: socket power (amd-smi) while sparse attention, dense attention and the "
-                         "MFMA probe each run back to back for --power-secs seconds")
+                         "MFMA probe each run back to back for --power-secs seconds. "
+                         "selection: precision / recall / F1 and kept attention mass of the estimated "
+                         "selections (round-robin variants, several S and tau) against the exact Top-tau "
+                         "selection, one JSON line per point")
     ap.add_argument("--power-secs", type=float, default=6.0)
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic_sparse_attn_llama_128k.json"))
@@ -119,6 +122,10 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
+    if args.mode == "selection":
+        for line in selection_report(args.workload):
+            print(json.dumps(line), flush=True)
+        return 0
     w = wl.WORKLOADS[args.workload]
     if w.fp32_inputs:
         log("pick a bf16 workload for the benchmark")
@@ -319,6 +326,73 @@ def mfma_ceiling() -> dict | None:
         runs.sort()
         res[name] = {"tflops": round(runs[1][0], 1), "clock_ghz": round(runs[1][1], 3)}
     return res
+
+
+SELECTION_POINTS = {
+    "llama_8k": [(16, 0.9)],
+    "llama_32k": [(s, t) for s in (8, 16, 32) for t in (0.8, 0.9, 0.95)],
+    "video_64k": [(16, 0.95)],
+    "llama_128k": [(16, 0.9)],
+}
+
+
+def selection_report(first_workload: str):
+    """Selections of the round-robin estimator (and its variants) scored
+    against the exact Top-tau selection on full attention's block masses."""
+    import torch
+
+    import dynamic_block_sparse_sample_amd as rra
+    from dynamic_block_sparse_sample_amd import workloads as wl
+    from dynamic_block_sparse_sample_amd.selection import selection_accuracy
+
+    names = list(SELECTION_POINTS)
+    if first_workload in names and first_workload != "llama_128k":
+        names = [first_workload]  # one workload when asked for a particular one
+    for name in names:
+        w = wl.WORKLOADS[name]
+        log(f"[selection] {name}: generating inputs")
+        q, k, _ = wl.make_inputs(w)
+        qd, kd = q.cuda(), k.cuda()
+        del q, k
+        p0 = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block, w.tau)
+        mass = rra.block_mass(p0, qd, kd)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        rra.block_mass(p0, qd, kd, mass=mass)
+        b.record()
+        torch.cuda.synchronize()
+        nb = p0.num_blocks
+        f_mass = 2 * 2.0 * w.head_dim * w.block * w.block * w.batch * w.num_heads * nb * (nb + 1) / 2
+        t_mass = a.elapsed_time(b)
+        exact = {}
+        for S, tau in SELECTION_POINTS[name]:
+            if tau not in exact:
+                pt = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, tau)
+                exact[tau] = rra.top_tau(pt, mass)[0]
+            variants = [("head", [(0, 0)]), ("hybrid", [(l0, 0) for l0 in range(S)]),
+                        ("layer", [(l0, 0) for l0 in range(S)]), ("none_first", [(0, 0)]),
+                        ("none_last", [(0, S - 1)])]
+            for label, settings in variants:
+                mode = label.split("_")[0]
+                acc = []
+                for layer, fixed in settings:
+                    p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block,
+                                        tau, rr_mode=mode, rr_layer=layer, rr_offset=fixed)
+                    sel = rra.estimate(p, qd, kd)
+                    acc.append(selection_accuracy(sel.mask, exact[tau], mass, tau))
+                keys = [kk for kk in acc[0] if kk not in ("tp", "fp", "fn")]
+                avg = {kk: round(sum(r[kk] for r in acc) / len(acc), 5) for kk in keys}
+                line = {"mode": "selection", "workload": name, "stride": S, "tau": tau, "rr": label,
+                        "layers_averaged": len(settings), **avg,
+                        "block_mass_ms": round(t_mass, 3),
+                        "block_mass_tflops": round(f_mass / (t_mass * 1e-3) / 1e12, 1)}
+                log(f"[selection] {name} S={S} tau={tau} {label}: F1 {avg['f1']:.4f} "
+                    f"kept {avg['mass_kept_mean']:.4f} density {avg['density_estimated']:.4f} "
+                    f"(exact {avg['density_exact']:.4f})")
+                yield line
+        del qd, kd, mass, exact
+        torch.cuda.empty_cache()
 
 
 def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     RRAError,
     Selection,
     alloc_workspace,
+    block_mass,
     block_scores,
     cast_f32_to_bf16,
     dense_attn,
@@ -25,7 +26,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "LIB_PATH", "Params", "RRAError", "Selection", "alloc_workspace", "block_scores", "cast_f32_to_bf16",
+    "LIB_PATH", "Params", "RRAError", "Selection", "alloc_workspace", "block_mass", "block_scores",
+    "cast_f32_to_bf16",
     "dense_attn", "estimate", "lib", "make_params", "sparse_attn", "status_str", "stride_aggregate",
     "top_tau", "validate", "workspace_size",
 ]

@@ -68,6 +68,7 @@ SIGNATURES = {
     "rra_block_scores": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_top_tau": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
     "rra_estimate": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "rra_block_mass": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P]),
     "rra_dense_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
 }
@@ -189,6 +190,19 @@ def block_scores(p: Params, q: torch.Tensor, kagg: torch.Tensor, score: torch.Te
     _check("rra_block_scores",
            lib().rra_block_scores(ctypes.byref(p), _ptr(q), _ptr(kagg), _ptr(score), _stream(stream)))
     return score
+
+
+def block_mass(p: Params, q: torch.Tensor, k: torch.Tensor, mass: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Exact block masses of full causal attention, float32 [Bz, H, Nb, Nb]."""
+    qs, ks, nb, _ = _shapes(p)
+    _need(q, "q", torch.bfloat16, qs)
+    _need(k, "k", torch.bfloat16, ks)
+    if mass is None:
+        mass = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+    _need(mass, "mass", torch.float32, (p.batch, p.num_heads, nb, nb))
+    _check("rra_block_mass", lib().rra_block_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(mass), _stream(stream)))
+    return mass
 
 
 def _selection_buffers(p: Params, device, mask=None, idx=None, cnt=None):

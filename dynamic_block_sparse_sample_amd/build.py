@@ -29,6 +29,7 @@ SOURCES = [
     "kernels/stride_aggregate.hip",
     "kernels/block_scores.hip",
     "kernels/top_tau.hip",
+    "kernels/block_mass.hip",
     "kernels/flash_attn.hip",
 ]
 PROBE_SOURCES = ["probe/mfma_rate.hip"]

@@ -82,6 +82,16 @@ rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, v
   return hip_status(err);
 }
 
+rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k, float* mass, void* stream) {
+  rra_status_t st = check(p);
+  if (st != RRA_OK) return st;
+  if (empty_problem(p)) return RRA_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(mass)) return RRA_ERR_INVALID_ARG;
+  const rra::Shape s = rra::shape_of(*p);
+  return hip_status(rra::launch_block_mass(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           mass, stream));
+}
+
 rra_status_t rra_sparse_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
                              const int32_t* idx, const int32_t* cnt, void* out, void* stream) {
   rra_status_t st = check(p);

@@ -140,6 +140,18 @@ rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, v
                           size_t workspace_bytes, uint8_t* mask, int32_t* idx, int32_t* cnt,
                           float* score, void* stream);
 
+/* Exact block masses of full causal attention, the reference the estimated
+ * block scores approximate (§3.2 with S = 1: every query sampled, every key
+ * its own stride; §3.3 Top-tau on it is the exact selection):
+ *   mass[b,h,I,J] = (1/Bk) * sum_{t in block I} sum_{u in block J, u <= t} p[t,u],
+ *   p[t,u] = softmax over u <= t of sm_scale * q_t . k_u,
+ * every row summing to 1, J > I written as 0.  mass is float32
+ * [Bz, H, Nb, Nb]; S, tau and the round-robin fields are not used.  bf16
+ * MFMA, float32 softmax and sums (two passes over the causal keys).  Used to
+ * score the estimator's selections (precision / recall against the exact
+ * Top-tau set, and the attention mass they keep). */
+rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k, float* mass, void* stream);
+
 /* Block-sparse causal flash attention (§4.1, prefill): for query t of
  * block I of head h,
  *   out[b,h,t] = sum_{u in A(t)} softmax_u(sm_scale * q_t . k_u) v_u,

@@ -69,6 +69,8 @@ __all__ = [
     "top_tau_row",
     "select_blocks",
     "estimate",
+    "exact_block_mass",
+    "exact_block_mass_row",
     "block_sparse_attention",
     "dense_attention",
     "attention_rows",
@@ -239,6 +241,40 @@ def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "b
                 s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale, prm.rr_mode, prm.rr_layer,
                                   prm.rr_fixed)
                 out[b, h] = pool_blocks(stride_softmax(s), prm.strides_per_block)
+    return out
+
+
+def exact_block_mass(q: np.ndarray, k: np.ndarray, prm: Params) -> np.ndarray:
+    """Block masses of full causal softmax attention: [Bz, H, Nb, Nb].
+
+    M*[I, J] = (1/Bk) * sum_{t in I} sum_{u in J, u <= t} p[t, u], with p the
+    causal softmax of sm_scale * q_t . k_u over u <= t.  This is what the
+    estimator's block score stands for (§3.2 with every query sampled and no
+    key aggregation); Top-tau on it (§3.3) is the exact selection the sampled
+    one is scored against.
+    """
+    nb = prm.num_blocks
+    out = np.zeros((prm.batch, prm.num_heads, nb, nb))
+    for b in range(prm.batch):
+        for h in range(prm.num_heads):
+            for i in range(nb):
+                out[b, h, i] = exact_block_mass_row(q, k, prm, b, h, i)
+    return out
+
+
+def exact_block_mass_row(q, k, prm: Params, b: int, h: int, row: int) -> np.ndarray:
+    """Row `row` of exact_block_mass for (b, h): [Nb], zero above the diagonal."""
+    bk = prm.block
+    n_keys = (row + 1) * bk
+    qb = np.asarray(q[b, h, row * bk:(row + 1) * bk], dtype=np.float64)
+    keys = np.asarray(k[b, h // prm.group, :n_keys], dtype=np.float64)
+    s = prm.scale * (qb @ keys.T)  # [Bk, (row+1) Bk]
+    t = row * bk + np.arange(bk)
+    s[np.arange(n_keys)[None, :] > t[:, None]] = -np.inf
+    e = np.exp(s - np.max(s, axis=1, keepdims=True))
+    p = e / np.sum(e, axis=1, keepdims=True)
+    out = np.zeros(prm.num_blocks)
+    out[: row + 1] = p.reshape(bk, row + 1, bk).sum(axis=(0, 2)) / bk
     return out
 
 

@@ -201,6 +201,27 @@ def test_stride_one_equals_textbook_block_attention_mass(block):
     np.testing.assert_allclose(m, ref, rtol=0, atol=1e-12)
 
 
+def test_exact_block_mass_is_textbook_block_attention_mass():
+    """exact_block_mass against torch's SDPA with V = block indicators (GQA,
+    H = 2 Hkv), and against the estimator's own block scores at S = 1."""
+    rng = np.random.default_rng(14)
+    L, d, H, Hkv, block = 192, 16, 4, 2, 32
+    prm = _prm(num_heads=H, num_kv_heads=Hkv, seq_len=L, head_dim=d, stride=1, block=block)
+    q = _bf16_values((1, H, L, d), rng, 2.0)
+    k = _bf16_values((1, Hkv, L, d), rng, 2.0)
+    m = orc.exact_block_mass(q, k, prm)
+    nb = L // block
+    ind = np.zeros((L, nb))
+    ind[np.arange(L), np.arange(L) // block] = 1.0
+    kr = torch.from_numpy(np.repeat(k, H // Hkv, axis=1))
+    vt = torch.from_numpy(np.broadcast_to(ind, (1, H, L, nb)).copy())
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kr, vt, is_causal=True, scale=1 / math.sqrt(d)).numpy()
+    np.testing.assert_allclose(m, o.reshape(1, H, nb, block, nb).mean(axis=3), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m, orc.block_scores(q, k, prm), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(m.sum(axis=-1), 1.0, atol=1e-12)
+
+
 def test_block_score_invariants():
     rng = np.random.default_rng(5)
     prm = _prm(num_heads=4, num_kv_heads=2, seq_len=512, head_dim=32, stride=8, block=64)
