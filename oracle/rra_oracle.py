@@ -94,6 +94,7 @@ class Params:
     rr_mode: str = "head"  # "head", "layer", "hybrid" or "none" (§4.3 ablation)
     rr_layer: int = 0  # layer index l for "layer" and "hybrid"
     rr_fixed: int = 0  # the offset for "none"
+    causal: bool = True  # False: every key visible to every query (encoder / generation use)
 
     @property
     def scale(self) -> float:
@@ -105,11 +106,11 @@ class Params:
 
     @property
     def num_strides(self) -> int:
-        return self.seq_len // self.stride
+        return -(-self.seq_len // self.stride)  # ceil: a last partial stride counts
 
     @property
     def num_blocks(self) -> int:
-        return self.seq_len // self.block
+        return -(-self.seq_len // self.block)  # ceil(L / B), §2.1
 
     @property
     def strides_per_block(self) -> int:
@@ -188,7 +189,10 @@ def aggregate_keys(k_head: np.ndarray, stride: int, kagg_round: str = "bf16") ->
     whose magnitudes span under 2^40), and /S is exact for a power-of-two S.
     """
     L, d = k_head.shape
-    sums = k_head.reshape(L // stride, stride, d).sum(axis=1)
+    ns = -(-L // stride)
+    padded = np.zeros((ns * stride, d))
+    padded[:L] = k_head  # a last partial stride sums the keys it has; the 1/S stays
+    sums = padded.reshape(ns, stride, d).sum(axis=1)
     mean = sums / stride
     if kagg_round == "bf16":
         return bf16_round(mean)
@@ -198,33 +202,56 @@ def aggregate_keys(k_head: np.ndarray, stride: int, kagg_round: str = "bf16") ->
 
 
 def stride_scores(q_head: np.ndarray, kagg: np.ndarray, stride: int, head: int,
-                  sm_scale: float, mode: str = "head", layer: int = 0, fixed: int = 0) -> np.ndarray:
+                  sm_scale: float, mode: str = "head", layer: int = 0, fixed: int = 0,
+                  causal: bool = True) -> np.ndarray:
     """s[i, j] = sm_scale * <Q[P(i, h)], Kagg[j]> for j <= i, -inf above.
 
     With Kagg the stride mean, sm_scale = 1/sqrt(d) gives the page's
     normalisation 1/(S*sqrt(d)) of Q_P(i,h) . sum_{t in stride j} K_t.
-    Every stride j <= i is visible, the diagonal stride included.
+    Every stride j <= i is visible, the diagonal stride included; every
+    stride when not causal.  Rows whose sampled position lies beyond the
+    sequence (a last partial stride) are NaN: that stride has no query.
     """
     ns = kagg.shape[0]
-    qs = q_head[rr_positions(ns, stride, head, mode, layer, fixed)]  # [Ns, d]
-    s = sm_scale * (qs @ kagg.T)
-    s[np.triu_indices(ns, k=1)] = -np.inf
+    pos = rr_positions(ns, stride, head, mode, layer, fixed)
+    have = pos < q_head.shape[0]  # a last partial stride may hold no sampled query: NaN row
+    s = np.full((ns, ns), np.nan)
+    s[have] = sm_scale * (q_head[pos[have]] @ kagg.T)
+    if causal:
+        upper = np.triu(np.ones((ns, ns), dtype=bool), k=1) & have[:, None]
+        s[upper] = -np.inf
     return s
 
 
 def stride_softmax(s: np.ndarray) -> np.ndarray:
-    """Softmax of every sampled query's row over its visible strides (§2.2)."""
-    m = np.max(s, axis=1, keepdims=True)
-    e = np.exp(s - m)
-    return e / np.sum(e, axis=1, keepdims=True)
+    """Softmax of every sampled query's row over its visible strides (§2.2).
+    Rows without a query (NaN) stay NaN."""
+    out = np.full(s.shape, np.nan)
+    ok = ~np.isnan(s).any(axis=1)
+    m = np.max(s[ok], axis=1, keepdims=True)
+    e = np.exp(s[ok] - m)
+    out[ok] = e / np.sum(e, axis=1, keepdims=True)
+    return out
 
 
 def pool_blocks(p: np.ndarray, strides_per_block: int) -> np.ndarray:
-    """M[I, J] = (1/r) * sum of p over the r x r stride cells of block (I, J)."""
+    """M[I, J] = (1/r_I) * sum of p over the stride cells of block (I, J).
+
+    r_I is the number of sampled queries block I holds: r = Bk / S for a
+    whole block, fewer for a last partial block; each row sums to 1.  A block
+    without any sampled query gets a zero row (no estimate).
+    """
     ns = p.shape[0]
     r = strides_per_block
-    nb = ns // r
-    return p.reshape(nb, r, nb, r).sum(axis=(1, 3)) / r
+    nb = -(-ns // r)
+    rows = ~np.isnan(p).any(axis=1)
+    pp = np.zeros((nb * r, nb * r))
+    pp[:ns, :ns][rows] = p[rows]
+    count = np.zeros(nb * r)
+    count[:ns] = rows
+    count = count.reshape(nb, r).sum(axis=1)
+    sums = pp.reshape(nb, r, nb, r).sum(axis=(1, 3))
+    return np.where(count[:, None] > 0, sums / np.maximum(count, 1)[:, None], 0.0)
 
 
 def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "bf16") -> np.ndarray:
@@ -239,7 +266,7 @@ def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "b
             for hh in range(prm.group):
                 h = g * prm.group + hh
                 s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale, prm.rr_mode, prm.rr_layer,
-                                  prm.rr_fixed)
+                                  prm.rr_fixed, prm.causal)
                 out[b, h] = pool_blocks(stride_softmax(s), prm.strides_per_block)
     return out
 
@@ -248,7 +275,8 @@ def exact_block_mass(q: np.ndarray, k: np.ndarray, prm: Params) -> np.ndarray:
     """Block masses of full causal softmax attention: [Bz, H, Nb, Nb].
 
     M*[I, J] = (1/Bk) * sum_{t in I} sum_{u in J, u <= t} p[t, u], with p the
-    causal softmax of sm_scale * q_t . k_u over u <= t.  This is what the
+    causal softmax of sm_scale * q_t . k_u over u <= t (over every key when
+    not causal; a last partial block averages over the queries it has).  This is what the
     estimator's block score stands for (§3.2 with every query sampled and no
     key aggregation); Top-tau on it (§3.3) is the exact selection the sampled
     one is scored against.
@@ -263,38 +291,48 @@ def exact_block_mass(q: np.ndarray, k: np.ndarray, prm: Params) -> np.ndarray:
 
 
 def exact_block_mass_row(q, k, prm: Params, b: int, h: int, row: int) -> np.ndarray:
-    """Row `row` of exact_block_mass for (b, h): [Nb], zero above the diagonal."""
-    bk = prm.block
-    n_keys = (row + 1) * bk
-    qb = np.asarray(q[b, h, row * bk:(row + 1) * bk], dtype=np.float64)
+    """Row `row` of exact_block_mass for (b, h): [Nb], zero above the diagonal
+    when causal.  The mean runs over the block's queries (fewer in a last
+    partial block), the sums over its keys inside the sequence."""
+    bk, L = prm.block, prm.seq_len
+    t = np.arange(row * bk, min((row + 1) * bk, L))
+    n_keys = min((row + 1) * bk, L) if prm.causal else L
+    qb = np.asarray(q[b, h, t], dtype=np.float64)
     keys = np.asarray(k[b, h // prm.group, :n_keys], dtype=np.float64)
-    s = prm.scale * (qb @ keys.T)  # [Bk, (row+1) Bk]
-    t = row * bk + np.arange(bk)
-    s[np.arange(n_keys)[None, :] > t[:, None]] = -np.inf
+    s = prm.scale * (qb @ keys.T)  # [rows, n_keys]
+    if prm.causal:
+        s[np.arange(n_keys)[None, :] > t[:, None]] = -np.inf
     e = np.exp(s - np.max(s, axis=1, keepdims=True))
     p = e / np.sum(e, axis=1, keepdims=True)
+    nbk = -(-n_keys // bk)
+    pp = np.zeros((t.size, nbk * bk))
+    pp[:, :n_keys] = p
     out = np.zeros(prm.num_blocks)
-    out[: row + 1] = p.reshape(bk, row + 1, bk).sum(axis=(0, 2)) / bk
+    out[:nbk] = pp.reshape(t.size, nbk, bk).sum(axis=(0, 2)) / t.size
     return out
 
 
 # ---------------------------------------------------------------------------
 # §3.3: Top-tau selection with last-query-block protection (§4.3).
 # ---------------------------------------------------------------------------
-def top_tau_row(m_row: np.ndarray, row: int, tau: float, protect: bool) -> np.ndarray:
+def top_tau_row(m_row: np.ndarray, row: int, tau: float, protect: bool, causal: bool = True) -> np.ndarray:
     """Selected key blocks (ascending) of query-block row `row`.
 
-    Candidates are J = 0..row (causal).  Keep all of them if tau >= 1 or the
-    row is protected; otherwise sort by (mass desc, J asc) and keep the
-    shortest prefix whose cumulative mass reaches tau times the row total.
+    Candidates are J = 0..row (causal) or every key block.  Keep all of them
+    if tau >= 1, the row is protected, or the row has no estimate (zero
+    total: a last partial block without a sampled query); otherwise sort by
+    (mass desc, J asc) and keep the shortest prefix whose cumulative mass
+    reaches tau times the row total.
     """
-    n = row + 1
+    n = row + 1 if causal else len(m_row)
     if tau >= 1.0 or protect:
         return np.arange(n, dtype=np.int64)
     vals = np.asarray(m_row[:n], dtype=np.float64)
+    total = np.sum(vals)
+    if not total > 0:
+        return np.arange(n, dtype=np.int64)
     order = np.lexsort((np.arange(n), -vals))  # last key is primary: mass desc, then J asc
     csum = np.cumsum(vals[order])
-    total = np.sum(vals)
     hit = np.nonzero(csum >= tau * total)[0]
     k_star = int(hit[0]) + 1 if hit.size else n
     return np.sort(order[:k_star])
@@ -309,7 +347,7 @@ def select_blocks(m: np.ndarray, prm: Params):
     for b in range(prm.batch):
         for h in range(prm.num_heads):
             for i in range(nb):
-                sel = top_tau_row(m[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1)
+                sel = top_tau_row(m[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1, prm.causal)
                 mask[b, h, i, sel] = 1
                 idx[b, h, i, : sel.size] = sel
                 cnt[b, h, i] = sel.size
@@ -327,10 +365,11 @@ def estimate(q, k, prm: Params, kagg_round: str = "bf16"):
 # §4.1: block-sparse causal prefill attention and its dense baseline.
 # ---------------------------------------------------------------------------
 def _attend(qb: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_pos: np.ndarray,
-            q_pos: np.ndarray, sm_scale: float) -> np.ndarray:
+            q_pos: np.ndarray, sm_scale: float, causal: bool = True) -> np.ndarray:
     """Exact softmax attention of queries qb over the given keys, causally masked."""
     s = sm_scale * (qb @ keys.T)
-    s[key_pos[None, :] > q_pos[:, None]] = -np.inf
+    if causal:
+        s[key_pos[None, :] > q_pos[:, None]] = -np.inf
     m = np.max(s, axis=1, keepdims=True)
     e = np.exp(s - m)
     return (e @ vals) / np.sum(e, axis=1, keepdims=True)
@@ -339,20 +378,24 @@ def _attend(qb: np.ndarray, keys: np.ndarray, vals: np.ndarray, key_pos: np.ndar
 def attention_rows(q, k, v, mask, prm: Params, b: int, h: int, row: int) -> np.ndarray:
     """Output rows of query block `row` of head h, restricted to mask[b, h, row].
 
-    Query t attends to keys u <= t lying in a selected key block.  Returns
-    [Bk, d] float64.
+    Query t attends to keys u <= t (any u when not causal) lying in a
+    selected key block and inside the sequence.  Returns [rows, d] float64,
+    rows = the block's tokens (fewer for a last partial block).
     """
-    bk = prm.block
+    bk, L = prm.block, prm.seq_len
     g = h // prm.group
-    sel = np.nonzero(np.asarray(mask[b, h, row][: row + 1]))[0]
+    n_cand = row + 1 if prm.causal else prm.num_blocks
+    sel = np.nonzero(np.asarray(mask[b, h, row][:n_cand]))[0]
     if sel.size == 0:
         raise ValueError("empty selection")
     key_pos = (sel[:, None] * bk + np.arange(bk)[None, :]).reshape(-1)
+    key_pos = key_pos[key_pos < L]
     q_pos = row * bk + np.arange(bk)
+    q_pos = q_pos[q_pos < L]
     qb = np.asarray(q[b, h, q_pos], dtype=np.float64)
     keys = np.asarray(k[b, g, key_pos], dtype=np.float64)
     vals = np.asarray(v[b, g, key_pos], dtype=np.float64)
-    return _attend(qb, keys, vals, key_pos, q_pos, prm.scale)
+    return _attend(qb, keys, vals, key_pos, q_pos, prm.scale, prm.causal)
 
 
 def block_sparse_attention(q, k, v, mask, prm: Params) -> np.ndarray:
@@ -362,13 +405,15 @@ def block_sparse_attention(q, k, v, mask, prm: Params) -> np.ndarray:
     for b in range(prm.batch):
         for h in range(prm.num_heads):
             for i in range(prm.num_blocks):
-                out[b, h, i * bk:(i + 1) * bk] = attention_rows(q, k, v, mask, prm, b, h, i)
+                o = attention_rows(q, k, v, mask, prm, b, h, i)
+                out[b, h, i * bk:i * bk + o.shape[0]] = o
     return out
 
 
 def dense_attention(q, k, v, prm: Params) -> np.ndarray:
-    """Dense causal attention: every causal key block selected."""
+    """Dense attention: every causal key block (every key block when not causal) selected."""
     nb = prm.num_blocks
-    full = np.broadcast_to(np.tril(np.ones((nb, nb), dtype=np.uint8)),
-                           (prm.batch, prm.num_heads, nb, nb))
-    return block_sparse_attention(q, k, v, full, prm)
+    full = np.ones((nb, nb), dtype=np.uint8)
+    if prm.causal:
+        full = np.tril(full)
+    return block_sparse_attention(q, k, v, np.broadcast_to(full, (prm.batch, prm.num_heads, nb, nb)), prm)

@@ -415,3 +415,112 @@ def test_tiny_planted_structure_is_found():
     rows = mask.reshape(-1, nb, nb)
     assert rows[:, :, 0].mean() >= 0.99  # the vertical column at token 0
     assert np.mean([rows[:, i, i].mean() for i in range(nb)]) >= 0.99  # the local diagonal
+
+
+# ---------------------------------------------------------------------------
+# ragged lengths (L not a multiple of the block) and non-causal attention
+# ---------------------------------------------------------------------------
+def _indicator_block_means(q, k, L, block, causal, H):
+    """Textbook block masses from torch SDPA: V = one-hot key-block indicators,
+    averaged over the queries each query block holds (fewer in a partial block)."""
+    nb = -(-L // block)
+    ind = np.zeros((L, nb))
+    ind[np.arange(L), np.arange(L) // block] = 1.0
+    kk = torch.from_numpy(np.repeat(k, H // k.shape[1], axis=1))
+    vt = torch.from_numpy(np.broadcast_to(ind, (1, H, L, nb)).copy())
+    o = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kk, vt, is_causal=causal, scale=1 / math.sqrt(q.shape[-1])).numpy()
+    out = np.zeros((1, H, nb, nb))
+    for i in range(nb):
+        out[0, :, i] = o[0, :, i * block:min((i + 1) * block, L)].mean(axis=1)
+    return out
+
+
+@pytest.mark.parametrize("L,causal", [(192, False), (200, True), (200, False), (161, True)])
+def test_stride_one_ragged_and_noncausal_are_textbook_block_masses(L, causal):
+    """S = 1 makes the estimator exact; with a ragged L the last block averages
+    over the queries it has, and without causality every key is visible."""
+    rng = np.random.default_rng(21)
+    H, Hkv, d, block = 4, 2, 16, 32
+    prm = _prm(num_heads=H, num_kv_heads=Hkv, seq_len=L, head_dim=d, stride=1, block=block, causal=causal)
+    q = _bf16_values((1, H, L, d), rng, 2.0)
+    k = _bf16_values((1, Hkv, L, d), rng, 2.0)
+    ref = _indicator_block_means(q, k, L, block, causal, H)
+    np.testing.assert_allclose(orc.block_scores(q, k, prm), ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.exact_block_mass(q, k, prm), ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ref.sum(axis=-1), 1.0, atol=1e-12)
+
+
+def test_partial_stride_aggregate_closed_form():
+    """A last partial stride sums the keys it has, times 1/S (exact fractions)."""
+    rng = np.random.default_rng(22)
+    k = _bf16_values((21, 4), rng)
+    kagg = orc.aggregate_keys(k, 8, "none")
+    assert kagg.shape == (3, 4)
+    for c in range(4):
+        assert Fraction(float(kagg[2, c])) == sum(Fraction(float(x)) for x in k[16:21, c]) / 8
+        assert Fraction(float(kagg[1, c])) == sum(Fraction(float(x)) for x in k[8:16, c]) / 8
+
+
+def test_ragged_block_without_sampled_query_keeps_every_candidate():
+    """L = 20, S = 8, Bk = 8: stride 2 holds tokens 16..19.  A fixed offset of 5
+    samples no query there, so block 2 has no estimate (zero row) and keeps
+    all its candidates; offset 3 samples token 19 and gets a normal row."""
+    rng = np.random.default_rng(23)
+    L, d = 20, 8
+    q = _bf16_values((1, 1, L, d), rng)
+    k = _bf16_values((1, 1, L, d), rng)
+    for fixed, has_row in ((5, False), (3, True)):
+        prm = _prm(num_heads=1, num_kv_heads=1, seq_len=L, head_dim=d, stride=8, block=8, tau=0.5,
+                   protect_last=False, rr_mode="none", rr_fixed=fixed)
+        assert orc.rr_positions(prm.num_strides, 8, 0, "none", 0, fixed).tolist() == [fixed, 8 + fixed, 16 + fixed]
+        m = orc.block_scores(q, k, prm)
+        assert m.shape == (1, 1, 3, 3)
+        np.testing.assert_allclose(m[0, 0, :2].sum(axis=-1), 1.0, atol=1e-12)
+        mask, idx, cnt = orc.select_blocks(m, prm)
+        if has_row:
+            assert abs(m[0, 0, 2].sum() - 1.0) < 1e-12
+        else:
+            assert np.all(m[0, 0, 2] == 0)
+            assert cnt[0, 0, 2] == 3 and mask[0, 0, 2].tolist() == [1, 1, 1]
+
+
+def test_top_tau_brute_force_noncausal_candidates():
+    """Without causality every key block of the row is a candidate."""
+    rng = np.random.default_rng(24)
+    for trial in range(100):
+        n = int(rng.integers(2, 9))
+        row = rng.dirichlet(np.full(n, 0.7))
+        tau = float(np.float32(rng.uniform(0.1, 0.95)))
+        sel = orc.top_tau_row(row, 0, tau, protect=False, causal=False)  # row 0: causal would allow J = 0 only
+        best = min(kk for kk in range(1, n + 1)
+                   if max(sum(row[list(c)]) for c in itertools.combinations(range(n), kk)) >= tau * row.sum())
+        assert len(sel) == best and row[sel].sum() >= tau * row.sum()
+        assert orc.top_tau_row(row, 0, tau, protect=True, causal=False).tolist() == list(range(n))
+
+
+@pytest.mark.parametrize("L,causal", [(256, False), (230, True), (230, False)])
+def test_ragged_and_noncausal_attention_match_sdpa(L, causal):
+    rng = np.random.default_rng(25)
+    H, Hkv, d, bk = 3, 1, 16, 32
+    nb = -(-L // bk)
+    prm = _prm(num_heads=H, num_kv_heads=Hkv, seq_len=L, head_dim=d, block=bk, causal=causal)
+    q = _bf16_values((1, H, L, d), rng, 2.0)
+    k = _bf16_values((1, Hkv, L, d), rng, 2.0)
+    v = _bf16_values((1, Hkv, L, d), rng)
+    kk, vv = torch.from_numpy(k).expand(1, H, L, d), torch.from_numpy(v).expand(1, H, L, d)
+    dense_ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kk, vv,
+                                                                 is_causal=causal).numpy()
+    np.testing.assert_allclose(orc.dense_attention(q, k, v, prm), dense_ref, rtol=0, atol=1e-12)
+    mask = (rng.random((1, H, nb, nb)) < 0.4).astype(np.uint8)
+    if causal:
+        mask = mask * np.tril(np.ones((nb, nb), dtype=np.uint8))
+    for h in range(H):
+        for i in range(nb):
+            if mask[0, h, i].sum() == 0:
+                mask[0, h, i, rng.integers(0, i + 1)] = 1
+    tok = torch.from_numpy(mask.astype(bool)).repeat_interleave(bk, 2).repeat_interleave(bk, 3)[..., :L, :L]
+    if causal:
+        tok &= torch.ones(L, L, dtype=torch.bool).tril()
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kk, vv, attn_mask=tok).numpy()
+    np.testing.assert_allclose(orc.block_sparse_attention(q, k, v, mask, prm), ref, rtol=0, atol=1e-12)
