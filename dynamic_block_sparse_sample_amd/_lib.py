@@ -51,11 +51,11 @@ class Params(ctypes.Structure):
 
     @property
     def num_blocks(self) -> int:
-        return self.seq_len // self.block
+        return -(-self.seq_len // self.block) if self.block > 0 else 0  # ceil: a last partial block counts
 
     @property
     def num_strides(self) -> int:
-        return self.seq_len // self.stride
+        return -(-self.seq_len // self.stride) if self.stride > 0 else 0
 
 
 SIGNATURES = {
@@ -155,9 +155,7 @@ def _need(t: torch.Tensor, name: str, dtype, shape):
 def _shapes(p: Params):
     q = (p.batch, p.num_heads, p.seq_len, p.head_dim)
     kv = (p.batch, p.num_kv_heads, p.seq_len, p.head_dim)
-    nb = p.seq_len // p.block if p.block > 0 else 0
-    ns = p.seq_len // p.stride if p.stride > 0 else 0
-    return q, kv, nb, ns
+    return q, kv, p.num_blocks, p.num_strides
 
 
 def cast_f32_to_bf16(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -17,7 +17,10 @@
 // double-buffered with the next sub-tile's global loads in registers.
 // Pass 1 forms each query's row max and denominator (base 2, float32); pass 2
 // recomputes the scores, normalises them and sums them per key block: in-lane,
-// over the wave, then over the waves through LDS.
+// over the wave, then over the waves through LDS.  Ragged lengths: key rows
+// past the end repeat row L-1 and are masked, queries past the end count for
+// nothing, and a last partial block averages over the queries it has.
+// Without causality every key inside the sequence is visible.
 #include <cmath>
 
 #include "../rra_internal.h"
@@ -42,7 +45,8 @@ template <int D, int BLK>
 __global__ __launch_bounds__((BLK / 32) * 64, 2) void block_mass_kernel(const uint16_t* __restrict__ q,
                                                                         const uint16_t* __restrict__ k,
                                                                         float* __restrict__ mass, int H, int Hkv,
-                                                                        int G, int L, int Nb, float c) {
+                                                                        int G, int L, int Nb, float c,
+                                                                        int causal) {
   using C = BmCfg<D, BLK>;
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][C::KT * C::PITCH];
   __shared__ float red[2][C::NW];
@@ -65,22 +69,26 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void block_mass_kernel(const ui
   const int col = lane & 31;
   const int half = lane >> 5;
   const int q_tok = I * BLK + wv * 32 + col;
+  const bool q_in = q_tok < L;
+  const int key_lim = causal ? q_tok : L - 1;  // last visible key
+  const int n_q = min(BLK, L - I * BLK);       // queries in block I
 
   bf16x8 qb[C::KC];
   {
-    const uint16_t* qrow = q + ((static_cast<int64_t>(b) * H + h) * L + q_tok) * D + half * 8;
+    const uint16_t* qrow = q + ((static_cast<int64_t>(b) * H + h) * L + (q_in ? q_tok : L - 1)) * D + half * 8;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) qb[kc] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kc * 16));
   }
   const uint16_t* kbase = k + static_cast<int64_t>(bg) * L * D;
-  const int nsub = (I + 1) * C::SUB;
+  const int nsub = (causal ? I + 1 : Nb) * C::SUB;
 
   auto load_regs = [&](int s, u32x4 (&r)[C::CPT]) {
     const int64_t key0 = static_cast<int64_t>(s) * C::KT;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
       const int ch = tid + i * C::NT;
-      r[i] = *reinterpret_cast<const u32x4*>(kbase + (key0 + ch / C::RC) * D + (ch % C::RC) * 8);
+      const int64_t key = min(key0 + ch / C::RC, static_cast<int64_t>(L - 1));  // rows past the end: row L-1
+      r[i] = *reinterpret_cast<const u32x4*>(kbase + key * D + (ch % C::RC) * 8);
     }
   };
   auto store_lds = [&](int buf, const u32x4 (&r)[C::CPT]) {
@@ -106,7 +114,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void block_mass_kernel(const ui
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = s * C::KT + 32 * tt + 8 * (e >> 2) + 4 * half + (e & 3);
-        x[16 * tt + e] = (key <= q_tok) ? acc[e] * c : -INFINITY;
+        x[16 * tt + e] = (key <= key_lim) ? acc[e] * c : -INFINITY;
       }
     }
   };
@@ -136,7 +144,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void block_mass_kernel(const ui
       __syncthreads();
     }
   }
-  const float inv = 1.0f / sum_halves(l);
+  const float inv = q_in ? 1.0f / sum_halves(l) : 0.0f;  // queries past the end count for nothing
 
   // ---- pass 2: normalised probabilities summed per key block ----
   float* mrow = mass + row * Nb;
@@ -169,18 +177,19 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void block_mass_kernel(const ui
         float tot = 0.0f;
 #pragma unroll
         for (int w = 0; w < C::NW; ++w) tot += red[J & 1][w];
-        mrow[J] = tot * (1.0f / BLK);
+        mrow[J] = tot / static_cast<float>(n_q);
       }
     }
   }
-  for (int J = I + 1 + tid; J < Nb; J += C::NT) mrow[J] = 0.0f;
+  if (causal)
+    for (int J = I + 1 + tid; J < Nb; J += C::NT) mrow[J] = 0.0f;
 }
 
 template <int D, int BLK>
 static void launch_bm(const Shape& s, const uint16_t* q, const uint16_t* k, float* mass, hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
   hipLaunchKernelGGL((block_mass_kernel<D, BLK>), dim3(static_cast<unsigned>(blocks)), dim3(BmCfg<D, BLK>::NT), 0,
-                     st, q, k, mass, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e);
+                     st, q, k, mass, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, s.causal ? 1 : 0);
 }
 
 int launch_block_mass(const Shape& s, const uint16_t* q, const uint16_t* k, float* mass, void* stream) {

@@ -13,6 +13,11 @@
 // a tile; the other 16 live in lane ^ 32.  Row statistics (max, sum) are then
 // per-lane, with one cross-half exchange at the end.
 //
+// Ragged lengths: a last partial stride may hold no sampled query for a head
+// (its lane contributes nothing) and a last partial block averages over the
+// sampled queries it holds (a zero row when it holds none).  Without
+// causality every stride and key block is visible.
+//
 // Two passes over the visible strides j <= i: pass 1 finds the row max and
 // the softmax denominator (online, base-2), pass 2 recomputes the scores,
 // normalises them and sums them into block cells
@@ -50,7 +55,8 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ kagg,
                                                           float* __restrict__ score, int H, int Hkv,
                                                           int G, int L, int S, int Ns, int Nb, int n_rt,
-                                                          int nbg, float c, int rr_step, int rr_shift) {
+                                                          int nbg, float c, int rr_step, int rr_shift,
+                                                          int causal) {
   constexpr int KC = D / 16;
   const int lane = threadIdx.x;
   const int col = lane & 31;
@@ -69,7 +75,14 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
   const int ii = rho % R;
   const int h = g * G + hh;
   const int i = I * R + ii;         // sampled stride
-  const int64_t pos = static_cast<int64_t>(i) * S + (rr_step * h + rr_shift) % S;
+  const int off = (rr_step * h + rr_shift) % S;
+  const int64_t pos = static_cast<int64_t>(i) * S + off;
+  // A last partial stride may hold no sampled query for this head (pos >= L).
+  const bool has_q = valid && pos < L;
+  // Sampled queries of block I for this head: r_I = R for a whole block, fewer
+  // (possibly 0) in a last partial block; the block row is their mean.
+  const int n_sampled = (L > off) ? (L - off + S - 1) / S : 0;
+  const int r_I = min(R, max(0, n_sampled - I * R));
 
   bf16x8 qb[KC];
   {
@@ -77,13 +90,14 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (valid) w = *reinterpret_cast<const u32x4*>(qrow + kc * 16);
+      if (has_q) w = *reinterpret_cast<const u32x4*>(qrow + kc * 16);
       qb[kc] = as_bf16x8(w);
     }
   }
   const uint16_t* kbase = kagg + static_cast<int64_t>(bg) * Ns * D + half * 8;
-  const int ntile = ((I + 1) * R + 31) / 32;
-  const int jmax = valid ? i : -1;  // visible strides: j <= i
+  const int nvis = causal ? (I + 1) * R : Nb * R;  // strides of the candidate blocks
+  const int ntile = (nvis + 31) / 32;
+  const int jmax = has_q ? (causal ? i : Ns - 1) : -1;  // visible strides: j <= i (all when not causal)
 
   // ---- pass 1: row max and denominator (base-2 logits) ----
   float m = -INFINITY, z = 0.0f;
@@ -121,9 +135,11 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
     m = mm;
     z = zt;
   }
-  const float invz = valid ? 1.0f / z : 0.0f;
-  const float inv_r = 1.0f / static_cast<float>(R);
+  const float invz = has_q ? 1.0f / z : 0.0f;
+  const float inv_r = (r_I > 0) ? 1.0f / static_cast<float>(r_I) : 0.0f;  // no sampled query: zero row
   float* srow_base = score + (static_cast<int64_t>(b) * H * Nb + I) * Nb;  // + h * Nb * Nb + J
+
+  const int jlast = causal ? I : Nb - 1;  // last key block of the row
 
   // ---- pass 2: probabilities pooled into block cells ----
   load_kagg_tile<D>(a_cur, kbase, min(col, Ns - 1));
@@ -155,7 +171,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
 #pragma unroll
         for (int u = 0; u < NJ; ++u) {
           const int J = jt * NJ + u;
-          if (J <= I) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
         }
       }
     } else {
@@ -179,7 +195,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
         for (int u = 0; u < NJL; ++u) {
           const int so = 8 * (u / PER) + 4 * half + R * (u % PER);  // first stride of the block in the tile
           const int J = jt * (32 / R) + so / R;
-          if (J <= I) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
         }
       }
     }
@@ -188,6 +204,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
   }
 
   // ---- zeros above the diagonal for the heads of this row tile ----
+  if (!causal) return;
   constexpr int HPT = 32 / R;  // heads per row tile
   for (int t = 0; t < HPT; ++t) {
     const int hz = rt * HPT + t;
@@ -205,7 +222,7 @@ static void launch_bs(const Shape& s, const uint16_t* q, const uint16_t* kagg, f
   const float c = s.scale * kLog2e;
   hipLaunchKernelGGL((block_scores_kernel<D, R>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, st, q, kagg,
                      score, s.H, s.Hkv, s.G, s.L, s.S, s.Ns, s.Nb, n_rt, nbg, c, s.rr_step,
-                     s.rr_shift);
+                     s.rr_shift, s.causal ? 1 : 0);
 }
 
 template <int D>

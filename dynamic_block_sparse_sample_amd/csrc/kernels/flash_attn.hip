@@ -35,6 +35,12 @@
 // the dominant term of a peaked row carries no bf16 rounding); O and l are
 // rescaled only on sub-tiles where some row's max increased.
 //
+// Ragged lengths (L not a multiple of the block): rows of K and V beyond the
+// sequence are never read (copies of a tail sub-tile repeat row L-1, whose
+// keys are masked), Q rows beyond it load row L-1 and are not stored.
+// Without causality every key block is a candidate and only keys beyond the
+// sequence are masked.
+//
 // Work order: KV groups in phases small enough for the memory-side cache;
 // inside a phase longest rows (largest I) first, each group's workgroups on a
 // fixed set of XCDs (workgroup w runs on XCD w mod 8), the heads of a group
@@ -126,7 +132,7 @@ template <int D, int BLK>
 __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
-    int Hkv, int G, int L, int Nb, float c, int gp) {
+    int Hkv, int G, int L, int Nb, float c, int gp, int causal) {
   using C = FaCfg<D, BLK>;
   // K and V rings of two sub-tiles each (K(t) in kb[t & 1], V(t) in vb[t & 1]),
   // in distinct LDS objects so every access names its buffer statically.
@@ -183,7 +189,8 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   // Q as the B operand of S^T = K Q^T: 8 consecutive channels per lane and chunk.
   bf16x8 qb[C::KC];
   {
-    const uint16_t* qrow = q + ((static_cast<int64_t>(b) * H + h) * L + q_tok) * D + half * 8;
+    const int64_t q_ld = q_tok < L ? q_tok : L - 1;  // rows beyond a ragged end: loaded, never stored
+    const uint16_t* qrow = q + ((static_cast<int64_t>(b) * H + h) * L + q_ld) * D + half * 8;
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc) qb[kc] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kc * 16));
   }
@@ -203,7 +210,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
 
   // The index list is read-only for the whole kernel: read it through the
   // constant address space so the uniform loads are scalar (s_load).
-  const int nblk = (idx == nullptr) ? I + 1 : ((const_i32_ptr)(cnt))[row];
+  const int nblk = (idx == nullptr) ? (causal ? I + 1 : Nb) : ((const_i32_ptr)(cnt))[row];
   const int n_sub = nblk * C::SUB;
   const_i32_ptr list = (idx == nullptr) ? nullptr : ((const_i32_ptr)(idx)) + row * Nb;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k) + static_cast<int64_t>(bg) * L * C::ROWB;
@@ -217,20 +224,39 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   // Global byte offset (inside a sub-tile) of the 16 bytes this lane copies in
   // each of its copy instructions; the same for K and V.
   int goff[C::IPW];
+  int grow[C::IPW];
 #pragma unroll
   for (int i = 0; i < C::IPW; ++i) {
     const int inst = wv * C::IPW + i;
     const int r = inst * C::ROWS_PER_INST + cp_row;
     const int chunk = cp_slot ^ (swz(r) & (C::RC - 1));
     goff[i] = r * C::ROWB + chunk * 16;
+    grow[i] = r;
   }
   // Copy sub-tile t of K or V (block J) into an LDS buffer: IPW instructions per wave.
   auto copy_tile = [&](const uint8_t* base, int t, int J, uint8_t* buf) {
     const int64_t key0 = static_cast<int64_t>(J) * BLK + (t % C::SUB) * C::KT;
     const uint8_t* gtile = base + key0 * C::ROWB;
     const uint32_t l0 = lds_addr(buf) + wv * C::IPW * 1024;
+    if (key0 + C::KT <= L) {
 #pragma unroll
-    for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gtile, goff[i], l0 + i * 1024);
+      for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gtile, goff[i], l0 + i * 1024);
+    } else {  // tail sub-tile of a ragged sequence: rows past the end repeat row L-1
+      // (the lane offsets are unsigned, so they stay >= 0: rebase on row L-1
+      // when the whole sub-tile lies past the end)
+      const int last = static_cast<int>(L - 1 - key0);
+      if (last >= 0) {
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i) {
+          const int over = grow[i] - last;
+          copy16_to_lds(gtile, over > 0 ? goff[i] - over * C::ROWB : goff[i], l0 + i * 1024);
+        }
+      } else {
+        const uint8_t* gend = base + static_cast<int64_t>(L - 1) * C::ROWB;
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gend, goff[i] - grow[i] * C::ROWB, l0 + i * 1024);
+      }
+    }
   };
 
   // LDS read offsets that do not depend on the sub-tile.
@@ -270,6 +296,10 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     }
   };
 
+  // The block whose keys need a mask, and the last visible key inside it.
+  const int mask_blk = causal ? I : ((L % BLK != 0) ? Nb - 1 : -1);
+  const int mask_lim = causal ? q_local : L - 1 - (Nb - 1) * BLK;
+
   // Pipeline over sub-tiles t = 0 .. n_sub-1 (block J(t) = block_of(t)).  K runs
   // one sub-tile ahead of V: iteration s computes S(s+1) = K(s+1) Q^T with the
   // MFMA unit while the VALU turns S(s) into probabilities, then O += V(s) P(s).
@@ -308,15 +338,16 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     }
     lds_barrier();  // V(s) and K(s+1) landed for every wave
 
-    // Causal mask of S(s) when it lies in the diagonal block (rare; own branch).
-    if (J_cur == I) {
+    // Mask of S(s) in the one block that needs it (rare; own branch): the
+    // diagonal block when causal, else the last block of a ragged sequence.
+    if (J_cur == mask_blk) {
       const int key_base = (s % C::SUB) * C::KT;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key_local = key_base + 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
-          if (key_local > q_local) st_cur[t][e] = -INFINITY;
+          if (key_local > mask_lim) st_cur[t][e] = -INFINITY;
         }
     }
 
@@ -422,6 +453,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   l = sum_halves(l);
   const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
   uint16_t* orow = out + ((static_cast<int64_t>(b) * H + h) * L + q_tok) * D;
+  if (q_tok >= L) return;  // past a ragged end
 #pragma unroll
   for (int ct = 0; ct < C::CT; ++ct) {
 #pragma unroll
@@ -453,7 +485,8 @@ static void launch_fa(const Shape& s, const uint16_t* q, const uint16_t* k, cons
                       const int32_t* cnt, uint16_t* out, hipStream_t st) {
   const int64_t blocks = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
   hipLaunchKernelGGL((flash_attn_kernel<D, BLK>), dim3(static_cast<unsigned>(blocks)), dim3(FaCfg<D, BLK>::NT), 0,
-                     st, q, k, v, idx, cnt, out, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, phase_groups(s));
+                     st, q, k, v, idx, cnt, out, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, phase_groups(s),
+                     s.causal ? 1 : 0);
 }
 
 int launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,

@@ -2,7 +2,10 @@
 // block protection of §4.3; the same minimal-cumulative-set rule as
 // XAttention's threshold selection).
 //
-// One 256-thread workgroup per row (b, h, I).  The I+1 causal block scores are
+// One 256-thread workgroup per row (b, h, I).  The candidates are the I+1
+// causal key blocks (every key block when not causal); a row with a zero total
+// (a last partial query block without a sampled query: no estimate) keeps them
+// all.  The candidates' block scores are
 // packed into 64-bit keys (inverted float bits << 32 | J), so one ascending
 // bitonic sort in LDS orders them by (score desc, J asc).  A float64 prefix
 // scan over the sorted scores finds k* = the first prefix reaching
@@ -64,7 +67,8 @@ __global__ __launch_bounds__(kTopThreads) void top_tau_kernel(const float* __res
                                                               uint8_t* __restrict__ mask,
                                                               int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ cnt, int Nb,
-                                                              double tau, int protect_last, int keep_all) {
+                                                              double tau, int protect_last, int keep_all,
+                                                              int causal) {
   __shared__ uint64_t keys[kMaxBlocks];
   __shared__ int flags[kMaxBlocks];
   __shared__ double dsh[kTopWaves];
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(kTopThreads) void top_tau_kernel(const float* __res
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const int I = static_cast<int>(row % Nb);
-  const int n = I + 1;
+  const int n = causal ? I + 1 : Nb;  // candidate key blocks
   const float* srow = score + row * Nb;
   uint8_t* mrow = mask + row * Nb;
   int32_t* irow = idx + row * Nb;
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kTopThreads) void top_tau_kernel(const float* __res
     }
   }
   const int fmin = block_min_int(first, ish);
-  const int kstar = (fmin == INT_MAX) ? n : fmin + 1;
+  const int kstar = (fmin == INT_MAX || !(total > 0.0)) ? n : fmin + 1;
 
   for (int p = tid; p < kstar; p += kTopThreads) flags[static_cast<uint32_t>(keys[p])] = 1;
   __syncthreads();
@@ -163,7 +167,7 @@ int launch_top_tau(const Shape& s, float tau, int protect_last, const float* sco
   const int keep_all = tau >= 1.0f ? 1 : 0;
   hipLaunchKernelGGL(top_tau_kernel, dim3(static_cast<unsigned>(rows)), dim3(kTopThreads), 0,
                      static_cast<hipStream_t>(stream), score, mask, idx, cnt, s.Nb, static_cast<double>(tau),
-                     protect_last, keep_all);
+                     protect_last, keep_all, s.causal ? 1 : 0);
   return static_cast<int>(hipGetLastError());
 }
 

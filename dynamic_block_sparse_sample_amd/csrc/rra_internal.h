@@ -15,10 +15,11 @@ constexpr int kMaxBlocks = 4096;
 struct Shape {
   int Bz, H, Hkv, L, d, S, Bk;
   int G;   // H / Hkv
-  int Ns;  // L / S
-  int Nb;  // L / Bk
+  int Ns;  // ceil(L / S)
+  int Nb;  // ceil(L / Bk)
   int r;   // Bk / S, strides per block
   float scale;
+  bool causal;
   // Sampled offset inside a stride for query head h: (rr_step * h + rr_shift) mod S.
   int rr_step;   // 1 for head / hybrid round-robin, 0 otherwise
   int rr_shift;  // in [0, S)

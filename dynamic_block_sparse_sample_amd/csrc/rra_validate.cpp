@@ -18,8 +18,11 @@ Shape shape_of(const rra_params_t& p) {
   s.S = p.stride;
   s.Bk = p.block;
   s.G = p.num_heads / (p.num_kv_heads > 0 ? p.num_kv_heads : 1);
-  s.Ns = p.seq_len / (p.stride > 0 ? p.stride : 1);
-  s.Nb = p.seq_len / (p.block > 0 ? p.block : 1);
+  const int Sd = p.stride > 0 ? p.stride : 1;
+  const int Bd = p.block > 0 ? p.block : 1;
+  s.Ns = (p.seq_len + Sd - 1) / Sd;  // a last partial stride counts
+  s.Nb = (p.seq_len + Bd - 1) / Bd;  // ceil(L / Bk), §2.1
+  s.causal = p.causal != 0;
   s.r = p.block / (p.stride > 0 ? p.stride : 1);
   s.scale = (p.sm_scale > 0.0f) ? p.sm_scale : 1.0f / std::sqrt(static_cast<float>(p.head_dim));
   const int S = p.stride > 0 ? p.stride : 1;
@@ -74,15 +77,16 @@ rra_status_t rra_validate(const rra_params_t* p) {
   if (p->rr_mode < RRA_RR_HEAD || p->rr_mode > RRA_RR_NONE) return RRA_ERR_INVALID_ARG;
   if (p->rr_layer < 0 || p->rr_offset < 0 || p->rr_offset >= p->stride) return RRA_ERR_INVALID_ARG;
   // Shapes the kernels are built for.
-  if (p->causal != 1) return RRA_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return RRA_ERR_UNSUPPORTED;
   if (p->block != 64 && p->block != 128) return RRA_ERR_UNSUPPORTED;
-  if (p->seq_len % p->block != 0) return RRA_ERR_UNSUPPORTED;
   const int r = p->block / p->stride;
   if (r > 32) return RRA_ERR_UNSUPPORTED;  // strides per block must fit one 32-wide MFMA tile
-  if (p->seq_len / p->block > rra::kMaxBlocks) return RRA_ERR_UNSUPPORTED;
+  const int64_t nb = (static_cast<int64_t>(p->seq_len) + p->block - 1) / p->block;
+  if (nb > rra::kMaxBlocks) return RRA_ERR_UNSUPPORTED;
   const int64_t elems_q = static_cast<int64_t>(p->batch) * p->num_heads * p->seq_len * p->head_dim;
   if (elems_q > (int64_t(1) << 40)) return RRA_ERR_UNSUPPORTED;
+  const int64_t strides = static_cast<int64_t>(p->batch) * p->num_kv_heads * ((p->seq_len + p->stride - 1) / p->stride);
+  if (strides >= (int64_t(1) << 31)) return RRA_ERR_UNSUPPORTED;
   return RRA_OK;
 }
 

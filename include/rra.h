@@ -18,8 +18,8 @@
  *  - Layouts are dense row-major:
  *        q, out   [Bz, H,   L, d]     bfloat16
  *        k, v     [Bz, Hkv, L, d]     bfloat16
- *        kagg     [Bz, Hkv, Ns, d]    bfloat16, Ns = L / S
- *        score    [Bz, H, Nb, Nb]     float32,  Nb = L / Bk
+ *        kagg     [Bz, Hkv, Ns, d]    bfloat16, Ns = ceil(L / S)
+ *        score    [Bz, H, Nb, Nb]     float32,  Nb = ceil(L / Bk) (§2.1)
  *        mask     [Bz, H, Nb, Nb]     uint8 (1 = key block selected)
  *        idx      [Bz, H, Nb, Nb]     int32, first cnt entries of each row valid
  *        cnt      [Bz, H, Nb]         int32
@@ -65,12 +65,13 @@ typedef enum rra_rr_mode {
   RRA_RR_NONE = 3
 } rra_rr_mode_t;
 
-/* Problem description (§2.1: Q, K of one head are L x d, split into blocks
- * of Bk tokens, with a finer sampling stride S; §3.3: threshold tau;
- * causal prefill, §4.1).  Supported: H % Hkv == 0; d in {64, 128};
- * Bk in {64, 128}; L % Bk == 0; Bk % S == 0 and Bk / S <= 32;
- * L / Bk <= 4096; 0 < tau <= 1; causal == 1; protect_last in {0, 1};
- * rr_mode in rra_rr_mode_t; rr_layer >= 0; 0 <= rr_offset < S.
+/* Problem description (§2.1: Q, K of one head are L x d, split into
+ * ceil(L / Bk) blocks of Bk tokens, the last one possibly partial, with a
+ * finer sampling stride S; §3.3: threshold tau; causal prefill, §4.1, or
+ * causal = 0 for attention without a causal mask).  Supported: H % Hkv == 0;
+ * d in {64, 128}; Bk in {64, 128}; Bk % S == 0 and Bk / S <= 32;
+ * ceil(L / Bk) <= 4096; 0 < tau <= 1; causal in {0, 1}; protect_last in
+ * {0, 1}; rr_mode in rra_rr_mode_t; rr_layer >= 0; 0 <= rr_offset < S.
  * A zero-filled tail (rr_mode = rr_layer = rr_offset = 0) is head-RR.
  * batch == 0 or seq_len == 0 is a valid empty problem: every entry point
  * returns RRA_OK without touching memory. */
@@ -83,7 +84,7 @@ typedef struct rra_params {
   int32_t stride;       /* S, sampling stride (§2.1)                       */
   int32_t block;        /* Bk, query and key block size (§2.1's B)         */
   float tau;            /* Top-tau threshold (§3.3); 1 keeps every block   */
-  int32_t causal;       /* must be 1                                       */
+  int32_t causal;       /* 1: causal (prefill); 0: every key visible       */
   int32_t protect_last; /* 1: the last query-block row keeps every causal
                            key block (§4.3, last query block protection)  */
   float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim)      */
@@ -109,27 +110,33 @@ rra_status_t rra_estimate_workspace_size(const rra_params_t* p, size_t* bytes);
 rra_status_t rra_cast_f32_to_bf16(const float* src, void* dst_bf16, int64_t n, void* stream);
 
 /* Stride key aggregation (§3.2: the sum of the key vectors of each stride,
- * normalised by 1/S): kagg[b,g,j,:] = bf16_rne( (sum_{t=jS}^{jS+S-1} k[b,g,t,:]) / S ).
- * The sum is formed exactly (float64) and rounded once to bf16. */
+ * normalised by 1/S): kagg[b,g,j,:] = bf16_rne( (sum_{t=jS}^{min(jS+S,L)-1} k[b,g,t,:]) / S ).
+ * The sum is formed exactly (float64) and rounded once to bf16; a last
+ * partial stride sums the keys it has (still divided by S). */
 rra_status_t rra_stride_aggregate(const rra_params_t* p, const void* k, void* kagg, void* stream);
 
 /* Round-robin sampled stride scores, stride softmax and block pooling
  * (§3.1, §3.2, §2.2 query independence).  For query head h the query of
  * stride i is taken at position P(i,h) = i*S + o(h), o(h) = h mod S for
  * head-RR (other strategies: rra_rr_mode_t); its scores
- * s[i,j] = sm_scale * <q[P(i,h)], kagg[j]> over strides j <= i are softmax
- * normalised per sampled query, and pooled:
- *   score[b,h,I,J] = (1/r) * sum_{i in block I} sum_{j in block J, j <= i} p[i,j],
- * r = Bk / S, so every row sums to 1.  Entries with J > I are written as 0. */
+ * s[i,j] = sm_scale * <q[P(i,h)], kagg[j]> over strides j <= i (every j
+ * when causal = 0) are softmax normalised per sampled query, and pooled:
+ *   score[b,h,I,J] = (1/r_I) * sum_{i in block I} sum_{j in block J, j <= i} p[i,j],
+ * r_I the number of sampled queries of block I (Bk / S, fewer in a last
+ * partial block, where P(i,h) >= L samples nothing), so every row sums to 1;
+ * a block with no sampled query gets a zero row.  Causal: entries with
+ * J > I are written as 0. */
 rra_status_t rra_block_scores(const rra_params_t* p, const void* q, const void* kagg, float* score,
                               void* stream);
 
 /* Adaptive Top-tau block selection (§3.3; same rule as XAttention's
- * threshold selection).  For each row (b,h,I): order J in [0, I] by
- * (score desc, J asc) and keep the shortest prefix whose cumulative score
- * reaches tau * (row total); keep every J <= I when tau >= 1 or when
- * protect_last is set and I == Nb - 1.  Writes the whole mask row (0 above
- * the diagonal), idx[b,h,I,0:cnt] strictly ascending, and cnt[b,h,I]. */
+ * threshold selection).  For each row (b,h,I): order the candidates J in
+ * [0, I] ([0, Nb) when causal = 0) by (score desc, J asc) and keep the
+ * shortest prefix whose cumulative score reaches tau * (row total); keep
+ * every candidate when tau >= 1, when protect_last is set and I == Nb - 1,
+ * or when the row total is 0 (no estimate).  Writes the whole mask row (0
+ * above the diagonal when causal), idx[b,h,I,0:cnt] strictly ascending, and
+ * cnt[b,h,I]. */
 rra_status_t rra_top_tau(const rra_params_t* p, const float* score, uint8_t* mask, int32_t* idx,
                          int32_t* cnt, void* stream);
 
@@ -143,28 +150,31 @@ rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, v
 /* Exact block masses of full causal attention, the reference the estimated
  * block scores approximate (§3.2 with S = 1: every query sampled, every key
  * its own stride; §3.3 Top-tau on it is the exact selection):
- *   mass[b,h,I,J] = (1/Bk) * sum_{t in block I} sum_{u in block J, u <= t} p[t,u],
+ *   mass[b,h,I,J] = (1/n_I) * sum_{t in block I} sum_{u in block J, u <= t} p[t,u],
  *   p[t,u] = softmax over u <= t of sm_scale * q_t . k_u,
- * every row summing to 1, J > I written as 0.  mass is float32
+ * n_I the tokens of block I (Bk, fewer in a last partial block), every row
+ * summing to 1, J > I written as 0 (causal = 0: every key u < L).  mass is float32
  * [Bz, H, Nb, Nb]; S, tau and the round-robin fields are not used.  bf16
  * MFMA, float32 softmax and sums (two passes over the causal keys).  Used to
  * score the estimator's selections (precision / recall against the exact
  * Top-tau set, and the attention mass they keep). */
 rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k, float* mass, void* stream);
 
-/* Block-sparse causal flash attention (§4.1, prefill): for query t of
+/* Block-sparse causal flash attention (§4.1, prefill): for query t < L of
  * block I of head h,
  *   out[b,h,t] = sum_{u in A(t)} softmax_u(sm_scale * q_t . k_u) v_u,
- *   A(t) = { u <= t : block(u) in idx[b,h,I,0:cnt[b,h,I]] }.
- * idx rows must be strictly ascending key-block indices in [0, I] with
- * 1 <= cnt <= I + 1 (rra_top_tau's output satisfies this; other lists are
- * the caller's responsibility).  bf16 MFMA, float32 accumulation and online
- * softmax; out is rounded to bf16. */
+ *   A(t) = { u <= t, u < L : block(u) in idx[b,h,I,0:cnt[b,h,I]] }
+ * (without u <= t when causal = 0).  idx rows must be strictly ascending
+ * key-block indices in [0, I] ([0, Nb) when causal = 0) with
+ * 1 <= cnt <= I + 1 (Nb) (rra_top_tau's output satisfies this; other lists
+ * are the caller's responsibility).  bf16 MFMA, float32 accumulation and
+ * online softmax; out is rounded to bf16. */
 rra_status_t rra_sparse_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
                              const int32_t* idx, const int32_t* cnt, void* out, void* stream);
 
-/* Dense causal flash attention: rra_sparse_attn with every causal key block
- * selected (the FlashAttention baseline of §4.1), same kernel. */
+/* Dense flash attention: rra_sparse_attn with every causal key block (every
+ * key block when causal = 0) selected (the FlashAttention baseline of
+ * §4.1), same kernel. */
 rra_status_t rra_dense_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
                             void* out, void* stream);
 

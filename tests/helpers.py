@@ -61,16 +61,20 @@ def compare_masks(gpu_mask, gpu_cnt, gpu_idx, m_oracle, prm: orc.Params, heads=N
         for h in heads:
             for i in range(nb):
                 checked += 1
-                n = i + 1
+                n = i + 1 if prm.causal else nb  # candidate key blocks
                 gsel = np.nonzero(gpu_mask[b, h, i, :n])[0]
                 assert np.all(gpu_mask[b, h, i, n:] == 0), "mask above the diagonal"
                 assert gpu_cnt[b, h, i] == gsel.size, "count does not match the mask"
                 assert np.array_equal(gpu_idx[b, h, i, :gsel.size], gsel), "index list is not the ascending mask"
-                osel = orc.top_tau_row(m_oracle[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1)
+                osel = orc.top_tau_row(m_oracle[b, h, i], i, prm.tau, prm.protect_last and i == nb - 1,
+                                       prm.causal)
                 if np.array_equal(gsel, osel):
                     continue
                 vals = m_oracle[b, h, i, :n]
                 T = vals.sum()
+                if not T > 0:
+                    bad.append((b, h, i, "row without an estimate must keep every candidate"))
+                    continue
                 order = _order(vals)
                 csum = np.cumsum(vals[order]) / T
                 ks = osel.size

@@ -91,9 +91,11 @@ def P(**kw):
     (dict(num_kv_heads=0), 1),
     (dict(head_dim=96), 2),
     (dict(block=256, stride=16), 2),
-    (dict(seq_len=8000), 2),  # L % Bk != 0
+    (dict(seq_len=8000), 0),  # ragged: Nb = ceil(L / Bk)
+    (dict(seq_len=1), 0),
+    (dict(seq_len=128 * 4096 + 1), 2),  # ceil(L / Bk) = 4097 blocks
     (dict(stride=2), 2),  # Bk / S = 64 > 32
-    (dict(causal=False), 2),
+    (dict(causal=False), 0),
     (dict(seq_len=128 * 4097), 2),  # more than 4096 blocks
     (dict(rr_mode="layer", rr_layer=31), 0),
     (dict(rr_mode="hybrid", rr_layer=7), 0),
@@ -122,6 +124,9 @@ def test_workspace_size_formula():
     r256 = lambda x: (x + 255) // 256 * 256
     assert rra.workspace_size(p) == r256(kagg) + r256(score)
     assert rra.workspace_size(P(batch=0)) == 0
+    # ragged: ceil counts (L = 8000: 63 blocks of 128, 500 strides of 16)
+    assert rra.workspace_size(P(seq_len=8000)) == r256(1 * 8 * 500 * 128 * 2) + r256(1 * 32 * 63 * 63 * 4)
+    assert rra.workspace_size(P(seq_len=8001)) == r256(1 * 8 * 501 * 128 * 2) + r256(1 * 32 * 63 * 63 * 4)
     with pytest.raises(rra.RRAError):
         rra.workspace_size(P(head_dim=96))
 

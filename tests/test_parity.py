@@ -255,9 +255,9 @@ def test_protect_last_flag_and_empty_problem():
 
 
 def test_invalid_arguments_raise():
-    p = rra.make_params(1, 4, 2, 1000, 128, 16, 128, 0.9)  # L % Bk != 0
-    q = torch.zeros(1, 4, 1000, 128, dtype=torch.bfloat16, device="cuda")
-    k = torch.zeros(1, 2, 1000, 128, dtype=torch.bfloat16, device="cuda")
+    p = rra.make_params(1, 4, 2, 1024, 96, 16, 128, 0.9)  # d = 96 is not built
+    q = torch.zeros(1, 4, 1024, 96, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 1024, 96, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(rra.RRAError) as ei:
         rra.dense_attn(p, q, k, k)
     assert ei.value.code == 2
