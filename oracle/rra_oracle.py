@@ -70,6 +70,7 @@ __all__ = [
     "select_blocks",
     "estimate",
     "exact_block_mass",
+    "xattn_block_scores",
     "exact_block_mass_row",
     "block_sparse_attention",
     "dense_attention",
@@ -268,6 +269,35 @@ def block_scores(q: np.ndarray, k: np.ndarray, prm: Params, kagg_round: str = "b
                 s = stride_scores(q[b, h], kagg, prm.stride, h, prm.scale, prm.rr_mode, prm.rr_layer,
                                   prm.rr_fixed, prm.causal)
                 out[b, h] = pool_blocks(stride_softmax(s), prm.strides_per_block)
+    return out
+
+
+def xattn_block_scores(q: np.ndarray, k: np.ndarray, prm: Params) -> np.ndarray:
+    """XAttention's antidiagonal block scores, for comparison: [Bz, H, Nb, Nb].
+
+    Inside each S x S cell (query stride i, key stride j) of the token score
+    matrix, the entries on the antidiagonal running from the lower left to the
+    upper right are summed (XA summary and key points; RR §2.2 describes it as
+    aggregation across different queries).  With the queries of stride i
+    concatenated in reverse order and the keys of stride j concatenated in
+    order, that sum is one dot product of length S*d.  Normalised by
+    1/(S*sqrt(d)) like RR §3.2's stride scores, softmax per query stride over
+    the key strides j <= i, pooled into blocks with 1/r exactly as
+    block_scores does.  Whole blocks and causal attention only.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    S, ns, nb, d = prm.stride, prm.num_strides, prm.num_blocks, prm.head_dim
+    if prm.seq_len % prm.block or not prm.causal:
+        raise ValueError("xattn_block_scores: whole blocks and causal attention only")
+    out = np.zeros((prm.batch, prm.num_heads, nb, nb))
+    for b in range(prm.batch):
+        for h in range(prm.num_heads):
+            qrev = q[b, h].reshape(ns, S, d)[:, ::-1, :].reshape(ns, S * d)
+            kcat = k[b, h // prm.group].reshape(ns, S * d)
+            a = (prm.scale / S) * (qrev @ kcat.T)
+            a[np.triu_indices(ns, k=1)] = -np.inf
+            out[b, h] = pool_blocks(stride_softmax(a), prm.strides_per_block)
     return out
 
 

@@ -524,3 +524,35 @@ def test_ragged_and_noncausal_attention_match_sdpa(L, causal):
         tok &= torch.ones(L, L, dtype=torch.bool).tril()
     ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kk, vv, attn_mask=tok).numpy()
     np.testing.assert_allclose(orc.block_sparse_attention(q, k, v, mask, prm), ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# XAttention's antidiagonal scores (the in-library comparison estimator)
+# ---------------------------------------------------------------------------
+def test_xattn_scores_are_literal_antidiagonal_sums():
+    """Brute force from the definition: sum the lower-left to upper-right
+    antidiagonal of every S x S cell of the full token score matrix, scale by
+    1/S, mask j > i, softmax per query stride, pool into blocks."""
+    rng = np.random.default_rng(31)
+    S, L, d, H, Hkv, block = 4, 64, 8, 2, 1, 16
+    prm = _prm(num_heads=H, num_kv_heads=Hkv, seq_len=L, head_dim=d, stride=S, block=block)
+    q = _bf16_values((1, H, L, d), rng, 2.0)
+    k = _bf16_values((1, Hkv, L, d), rng, 2.0)
+    got = orc.xattn_block_scores(q, k, prm)
+    ns, nb, r = L // S, L // block, block // S
+    for h in range(H):
+        full = (q[0, h] @ k[0, 0].T) / math.sqrt(d)
+        a = np.full((ns, ns), -np.inf)
+        for i in range(ns):
+            for j in range(i + 1):
+                a[i, j] = sum(full[i * S + (S - 1 - o), j * S + o] for o in range(S)) / S
+        p = np.exp(a - a.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        m = np.zeros((nb, nb))
+        for I in range(nb):
+            for J in range(nb):
+                m[I, J] = p[I * r:(I + 1) * r, J * r:(J + 1) * r].sum() / r
+        np.testing.assert_allclose(got[0, h], m, rtol=0, atol=1e-12)
+    # S = 1: the antidiagonal is the single entry, so XAttention = exact block masses
+    p1 = _prm(num_heads=H, num_kv_heads=Hkv, seq_len=L, head_dim=d, stride=1, block=block)
+    np.testing.assert_allclose(orc.xattn_block_scores(q, k, p1), orc.exact_block_mass(q, k, p1), atol=1e-12)
