@@ -281,6 +281,7 @@ def main(argv=None) -> int:
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": f_sel, "avg_launch_ms": round(t_sp, 4)},
     }
+    line["pattern_search_vs_xattn"] = pattern_search_comparison(w, qd, kd)
     ceil = mfma_ceiling()
     if ceil is not None:
         ceil["sparse_attn_frac_of_random_operand_rate"] = round(achieved / ceil["random_operands"]["tflops"], 4)
@@ -336,6 +337,61 @@ SELECTION_POINTS = {
 }
 
 
+def xattn_supported(p) -> bool:
+    """Shapes rra_xattn_block_scores is built for."""
+    return (p.seq_len % p.block == 0 and p.causal == 1
+            and (p.block, p.stride) in ((128, 16), (128, 8), (128, 4), (64, 8), (64, 4)))
+
+
+def pattern_search_comparison(w, qd, kd, reps=5) -> dict:
+    """Pattern-search time of the round-robin estimator (aggregation, scores,
+    Top-tau) against XAttention's antidiagonal estimator (scores, Top-tau) on
+    the same inputs, at the workload's S and at S = 8 (the pages' setting)."""
+    import torch
+
+    import dynamic_block_sparse_sample_amd as rra
+
+    res = {}
+    for S in sorted({w.stride, 8}, reverse=True):
+        p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, w.tau)
+        if not xattn_supported(p):
+            continue
+        ws = rra.alloc_workspace(p, qd.device)
+        sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
+        score = torch.empty((p.batch, p.num_heads, p.num_blocks, p.num_blocks), dtype=torch.float32,
+                            device=qd.device)
+        xa_sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
+
+        def rr():
+            rra.estimate(p, qd, kd, workspace=ws, out=sel)
+
+        def xa():
+            rra.xattn_block_scores(p, qd, kd, score=score)
+            rra.top_tau(p, score, xa_sel.mask, xa_sel.idx, xa_sel.cnt)
+
+        times = {}
+        for name, fn in (("rr", rr), ("xattn", xa)):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times[name] = a.elapsed_time(b) / reps
+        dens = lambda c: float(c.sum()) / (p.batch * p.num_heads * p.num_blocks * (p.num_blocks + 1) / 2)  # noqa: E731
+        ns = p.num_strides
+        res[f"S{S}"] = {
+            "rr_estimate_ms": round(times["rr"], 4), "xattn_estimate_ms": round(times["xattn"], 4),
+            "rr_time_saving_vs_xattn": round(1.0 - times["rr"] / times["xattn"], 4),
+            "rr_density": round(dens(sel.cnt), 5), "xattn_density": round(dens(xa_sel.cnt), 5),
+            "rr_score_gflop": round(2.0 * w.head_dim * w.batch * w.num_heads * ns * (ns + 1) / 2 / 1e9, 1),
+            "xattn_score_gflop": round(2.0 * S * w.head_dim * w.batch * w.num_heads * ns * (ns + 1) / 2 / 1e9, 1),
+        }
+    return res
+
+
 def selection_report(first_workload: str):
     """Selections of the round-robin estimator (and its variants) scored
     against the exact Top-tau selection on full attention's block masses."""
@@ -370,6 +426,17 @@ def selection_report(first_workload: str):
             if tau not in exact:
                 pt = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, tau)
                 exact[tau] = rra.top_tau(pt, mass)[0]
+            pt = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, tau)
+            if rra.validate(pt) == 0 and xattn_supported(pt):
+                xa_mask = rra.top_tau(pt, rra.xattn_block_scores(pt, qd, kd))[0]
+                r = selection_accuracy(xa_mask, exact[tau], mass, tau)
+                keys = [kk for kk in r if kk not in ("tp", "fp", "fn")]
+                line = {"mode": "selection", "workload": name, "stride": S, "tau": tau, "rr": "xattn_antidiagonal",
+                        "layers_averaged": 1, **{kk: round(r[kk], 5) for kk in keys},
+                        "block_mass_ms": round(t_mass, 3),
+                        "block_mass_tflops": round(f_mass / (t_mass * 1e-3) / 1e12, 1)}
+                log(f"[selection] {name} S={S} tau={tau} xattn: F1 {r['f1']:.4f} kept {r['mass_kept_mean']:.4f}")
+                yield line
             variants = [("head", [(0, 0)]), ("hybrid", [(l0, 0) for l0 in range(S)]),
                         ("layer", [(l0, 0) for l0 in range(S)]), ("none_first", [(0, 0)]),
                         ("none_last", [(0, S - 1)])]

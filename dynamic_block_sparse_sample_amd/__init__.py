@@ -23,11 +23,12 @@ from ._lib import (  # noqa: F401
     top_tau,
     validate,
     workspace_size,
+    xattn_block_scores,
 )
 
 __all__ = [
     "LIB_PATH", "Params", "RRAError", "Selection", "alloc_workspace", "block_mass", "block_scores",
     "cast_f32_to_bf16",
     "dense_attn", "estimate", "lib", "make_params", "sparse_attn", "status_str", "stride_aggregate",
-    "top_tau", "validate", "workspace_size",
+    "top_tau", "validate", "workspace_size", "xattn_block_scores",
 ]

@@ -69,6 +69,7 @@ SIGNATURES = {
     "rra_top_tau": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
     "rra_estimate": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P]),
     "rra_block_mass": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
+    "rra_xattn_block_scores": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P]),
     "rra_dense_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
 }
@@ -201,6 +202,20 @@ def block_mass(p: Params, q: torch.Tensor, k: torch.Tensor, mass: torch.Tensor |
     _need(mass, "mass", torch.float32, (p.batch, p.num_heads, nb, nb))
     _check("rra_block_mass", lib().rra_block_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(mass), _stream(stream)))
     return mass
+
+
+def xattn_block_scores(p: Params, q: torch.Tensor, k: torch.Tensor, score: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """XAttention's antidiagonal block scores (the comparison estimator), float32 [Bz, H, Nb, Nb]."""
+    qs, ks, nb, _ = _shapes(p)
+    _need(q, "q", torch.bfloat16, qs)
+    _need(k, "k", torch.bfloat16, ks)
+    if score is None:
+        score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+    _need(score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
+    _check("rra_xattn_block_scores",
+           lib().rra_xattn_block_scores(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(score), _stream(stream)))
+    return score
 
 
 def _selection_buffers(p: Params, device, mask=None, idx=None, cnt=None):

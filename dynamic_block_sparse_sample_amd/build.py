@@ -30,6 +30,7 @@ SOURCES = [
     "kernels/block_scores.hip",
     "kernels/top_tau.hip",
     "kernels/block_mass.hip",
+    "kernels/xattn_scores.hip",
     "kernels/flash_attn.hip",
 ]
 PROBE_SOURCES = ["probe/mfma_rate.hip"]

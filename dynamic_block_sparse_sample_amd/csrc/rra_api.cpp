@@ -82,6 +82,22 @@ rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, v
   return hip_status(err);
 }
 
+rra_status_t rra_xattn_block_scores(const rra_params_t* p, const void* q, const void* k, float* score,
+                                    void* stream) {
+  rra_status_t st = check(p);
+  if (st != RRA_OK) return st;
+  // Built for whole blocks, causal attention and (Bk, S) in {(128, 16), (128, 8), (128, 4), (64, 8), (64, 4)}.
+  const bool shape_ok = (p->seq_len % p->block == 0) && p->causal == 1 &&
+                        ((p->block == 128 && (p->stride == 16 || p->stride == 8 || p->stride == 4)) ||
+                         (p->block == 64 && (p->stride == 8 || p->stride == 4)));
+  if (!shape_ok) return RRA_ERR_UNSUPPORTED;
+  if (empty_problem(p)) return RRA_OK;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(score)) return RRA_ERR_INVALID_ARG;
+  const rra::Shape s = rra::shape_of(*p);
+  return hip_status(rra::launch_xattn_scores(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                             score, stream));
+}
+
 rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k, float* mass, void* stream) {
   rra_status_t st = check(p);
   if (st != RRA_OK) return st;

@@ -38,6 +38,7 @@ int launch_block_scores(const Shape& s, const uint16_t* q, const uint16_t* kagg,
                         void* stream);
 int launch_top_tau(const Shape& s, float tau, int protect_last, const float* score, uint8_t* mask,
                    int32_t* idx, int32_t* cnt, void* stream);
+int launch_xattn_scores(const Shape& s, const uint16_t* q, const uint16_t* k, float* score, void* stream);
 int launch_block_mass(const Shape& s, const uint16_t* q, const uint16_t* k, float* mass, void* stream);
 int launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const int32_t* idx, const int32_t* cnt, uint16_t* out, void* stream);

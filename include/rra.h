@@ -147,6 +147,20 @@ rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, v
                           size_t workspace_bytes, uint8_t* mask, int32_t* idx, int32_t* cnt,
                           float* score, void* stream);
 
+/* XAttention's antidiagonal block scores, the comparison estimator for
+ * pattern-search time (RR §2.2, §4.2; XAttention summary): inside each S x S
+ * cell the lower-left to upper-right antidiagonal of the token scores is
+ * summed,
+ *   a[i,j] = (sm_scale / S) * sum_{o<S} q[b,h,iS+S-1-o] . k[b,g,jS+o],
+ * then softmax per query stride over j <= i and pooled exactly as
+ * rra_block_scores does (1/r, r = Bk / S); rows sum to 1, J > I is 0.
+ * Run rra_top_tau on the result for XAttention's selection.  Built for
+ * L % Bk == 0, causal == 1 and (Bk, S) in {(128,16), (128,8), (128,4),
+ * (64,8), (64,4)}; other valid shapes return RRA_ERR_UNSUPPORTED.  The
+ * round-robin fields are not used. */
+rra_status_t rra_xattn_block_scores(const rra_params_t* p, const void* q, const void* k, float* score,
+                                    void* stream);
+
 /* Exact block masses of full causal attention, the reference the estimated
  * block scores approximate (§3.2 with S = 1: every query sampled, every key
  * its own stride; §3.3 Top-tau on it is the exact selection):

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = rra.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -148,6 +148,10 @@ def test_entry_points_reject_null_and_misaligned_pointers_without_launching():
     assert lib.rra_block_mass(by(p), fake, null, fake, s) == 1
     assert lib.rra_block_mass(by(p), fake, fake, odd, s) == 1
     assert lib.rra_block_mass(by(P(head_dim=96)), fake, fake, fake, s) == 2
+    assert lib.rra_xattn_block_scores(by(p), null, fake, fake, s) == 1
+    assert lib.rra_xattn_block_scores(by(P(stride=32)), fake, fake, fake, s) == 2  # r = 4: not built
+    assert lib.rra_xattn_block_scores(by(P(seq_len=8000)), fake, fake, fake, s) == 2  # ragged
+    assert lib.rra_xattn_block_scores(by(P(causal=False)), fake, fake, fake, s) == 2
     assert lib.rra_cast_f32_to_bf16(null, fake, 16, s) == 1
     assert lib.rra_cast_f32_to_bf16(fake, fake, -1, s) == 1
     assert lib.rra_cast_f32_to_bf16(null, null, 0, s) == 0  # nothing to do
@@ -172,3 +176,4 @@ def test_empty_problem_is_a_no_op_even_with_null_pointers():
     assert lib.rra_block_scores(by(p), None, None, None, None) == 0
     assert lib.rra_top_tau(by(p), None, None, None, None, None) == 0
     assert lib.rra_block_mass(by(p), None, None, None, None) == 0
+    assert lib.rra_xattn_block_scores(by(p), None, None, None, None) == 0
