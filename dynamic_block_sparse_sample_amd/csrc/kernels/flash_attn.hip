@@ -46,6 +46,8 @@
 // fixed set of XCDs (workgroup w runs on XCD w mod 8), the heads of a group
 // adjacent so that they stream the same K/V through one L2.
 #include <cmath>
+#include <type_traits>
+#include <utility>
 
 #include "../rra_internal.h"
 #include "rra_device.h"
@@ -85,21 +87,34 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 16 bytes per lane from global memory (gbase + voff) into LDS at
-// lds + 16 * lane (global_load_lds_dwordx4, saddr form).  Issued from inline
-// asm so that the compiler does not tie later LDS reads of the other pipeline
-// stage to this copy with a full vmcnt wait; completion is tracked explicitly
-// with wait_vmcnt.  m0 (the LDS base) is saved and restored.
+// lds + OFF + 16 * lane (global_load_lds_dwordx4, saddr form).  Issued from
+// inline asm so that the compiler does not tie later LDS reads of the other
+// pipeline stage to this copy with a full vmcnt wait; completion is tracked
+// explicitly with wait_vmcnt.  m0 (the LDS address) is formed from one base
+// register and an immediate, so the copies of a tile share one SGPR, and is
+// saved and restored.
+template <int OFF>
 __device__ __forceinline__ void copy16_to_lds(const uint8_t* gbase, int voff, uint32_t lds) {
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_add_u32 m0, %3, %4\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(gbase), "s"(lds)
-      : "memory");
+      : "v"(voff), "s"(gbase), "s"(lds), "i"(OFF)
+      : "memory", "scc");
+}
+
+// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N-1>), unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -235,26 +250,30 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   }
   // Copy sub-tile t of K or V (block J) into an LDS buffer: IPW instructions per wave.
   auto copy_tile = [&](const uint8_t* base, int t, int J, uint8_t* buf) {
-    const int64_t key0 = static_cast<int64_t>(J) * BLK + (t % C::SUB) * C::KT;
-    const uint8_t* gtile = base + key0 * C::ROWB;
+    const int key0 = J * BLK + (t % C::SUB) * C::KT;  // < L < 2^31
+    const uint8_t* gtile = base + static_cast<int64_t>(key0) * C::ROWB;
     const uint32_t l0 = lds_addr(buf) + wv * C::IPW * 1024;
     if (key0 + C::KT <= L) {
-#pragma unroll
-      for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gtile, goff[i], l0 + i * 1024);
+      static_for<C::IPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        copy16_to_lds<i * 1024>(gtile, goff[i], l0);
+      });
     } else {  // tail sub-tile of a ragged sequence: rows past the end repeat row L-1
       // (the lane offsets are unsigned, so they stay >= 0: rebase on row L-1
       // when the whole sub-tile lies past the end)
-      const int last = static_cast<int>(L - 1 - key0);
+      const int last = L - 1 - key0;
       if (last >= 0) {
-#pragma unroll
-        for (int i = 0; i < C::IPW; ++i) {
+        static_for<C::IPW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
           const int over = grow[i] - last;
-          copy16_to_lds(gtile, over > 0 ? goff[i] - over * C::ROWB : goff[i], l0 + i * 1024);
-        }
+          copy16_to_lds<i * 1024>(gtile, over > 0 ? goff[i] - over * C::ROWB : goff[i], l0);
+        });
       } else {
         const uint8_t* gend = base + static_cast<int64_t>(L - 1) * C::ROWB;
-#pragma unroll
-        for (int i = 0; i < C::IPW; ++i) copy16_to_lds(gend, goff[i] - grow[i] * C::ROWB, l0 + i * 1024);
+        static_for<C::IPW>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          copy16_to_lds<i * 1024>(gend, goff[i] - grow[i] * C::ROWB, l0);
+        });
       }
     }
   };
@@ -305,7 +324,9 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
   // MFMA unit while the VALU turns S(s) into probabilities, then O += V(s) P(s).
   // Copies issued in iteration s: V(s+1) and K(s+2), into the buffers that held
   // V(s-1) and K(s), both consumed before the previous closing barrier.
-  floatx16 st_cur[2];
+  // Scores of the current and the next sub-tile, swapped between the two
+  // unrolled steps of the loop (no register copies).
+  floatx16 st_a[2], st_b[2];
   int J_cur = 0, J_n1 = 0;
   if (n_sub > 0) {
     J_cur = block_of(0);
@@ -319,10 +340,11 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
       wait_vmcnt<C::IPW>();
     }
     lds_barrier();  // K(0) landed for every wave
-    qk(kb0, st_cur);
+    qk(kb0, st_a);
   }
 
-  auto step = [&](int s, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext) {
+  auto step = [&](int s, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext,
+                  floatx16 (&st_cur)[2], floatx16 (&st_next)[2]) {
     // kcur = K(s+1), vcur = V(s); V(s+1) -> vnext, K(s+2) -> knext.
     int J_n2 = J_n1;
     if (s + 2 < n_sub) {
@@ -366,7 +388,6 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     // K fragment four MFMAs ahead; sched_barrier keeps the chunks in order so
     // the MFMA unit and the VALU work side by side.  (For the last sub-tile the
     // product re-reads a stale K buffer; its result is unused.)
-    floatx16 st_next[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -439,14 +460,12 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_reads_done_barrier();  // every wave is done with K(s+1)'s and V(s)'s buffers
-#pragma unroll
-    for (int t = 0; t < 2; ++t) st_cur[t] = st_next[t];
     J_cur = J_n1;
     J_n1 = J_n2;
   };
   for (int s = 0; s < n_sub; s += 2) {
-    step(s, kb1, vb0, kb0, vb1);
-    if (s + 1 < n_sub) step(s + 1, kb0, vb1, kb1, vb0);
+    step(s, kb1, vb0, kb0, vb1, st_a, st_b);
+    if (s + 1 < n_sub) step(s + 1, kb0, vb1, kb1, vb0, st_b, st_a);
   }
 
   // ---- normalise and store: lane holds 4 consecutive channels per group ----
