@@ -341,6 +341,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     }
     lds_barrier();  // K(0) landed for every wave
     qk(kb0, st_a);
+    lds_reads_done_barrier();  // every wave has read K(0) before step 0 refills kb0 with K(2)
   }
 
   auto step = [&](int s, const uint8_t* kcur, const uint8_t* vcur, uint8_t* knext, uint8_t* vnext,
