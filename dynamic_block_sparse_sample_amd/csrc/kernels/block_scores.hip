@@ -2,8 +2,9 @@
 // (RRAttention §3.1 query sampling with head round-robin, §3.2 stride-level
 // importance estimation, §2.2 query independence).
 //
-// One wave per (batch, KV group g, query block I, row tile).  A row tile holds
-// 32 sampled queries: strides i of block I for the G query heads of group g,
+// One workgroup of four waves per (batch, KV group g, four consecutive query
+// blocks, row tile); wave w takes query block I0 - w.  A row tile holds 32
+// sampled queries: strides i of block I for the G query heads of group g,
 // taken at positions P(i,h) = i*S + o(h), o(h) = (rr_step * h + rr_shift) mod S
 // (head round-robin: h mod S; the layer / hybrid / fixed variants of the
 // §4.3 ablation change only o).  The wave computes the
@@ -22,23 +23,19 @@
 // the softmax denominator (online, base-2), pass 2 recomputes the scores,
 // normalises them and sums them into block cells
 //   score[b,h,I,J] = (1/r) sum_{i in I} sum_{j in J, j <= i} p[i,j]
-// with in-lane adds plus cross-lane xor shuffles over the r queries of a head.
-// Kagg tiles are read straight from L2 (16 bytes per lane per chunk, prefetched
-// one tile ahead); the aggregated keys of one KV head are 1/S of K and stay
-// cache-resident.
+// with in-lane adds plus DPP / permlane sums over the r queries of a head.
+// Kagg tiles (32 aggregated keys) are staged once per workgroup in LDS, rows
+// padded by 16 bytes so the A-operand reads of 32 rows are free of bank
+// conflicts, double-buffered with the next tile's loads in registers: the
+// four waves share every tile, a quarter of the L2 traffic of one wave per
+// query block (which bound this kernel).
+#include <climits>
 #include <cmath>
 
 #include "../rra_internal.h"
 #include "rra_device.h"
 
 namespace rra {
-
-template <int D>
-__device__ __forceinline__ void load_kagg_tile(u32x4 (&a)[D / 16], const uint16_t* kbase, int jrow) {
-  const uint16_t* p = kbase + static_cast<int64_t>(jrow) * D;
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(p + kc * 16);
-}
 
 template <int D>
 __device__ __forceinline__ floatx16 tile_mma(const u32x4 (&a)[D / 16], const bf16x8 (&qb)[D / 16]) {
@@ -50,27 +47,39 @@ __device__ __forceinline__ floatx16 tile_mma(const u32x4 (&a)[D / 16], const bf1
   return acc;
 }
 
+constexpr int kBsWaves = 4;  // query blocks (waves) per workgroup
+
 template <int D, int R>
-__global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ kagg,
                                                           float* __restrict__ score, int H, int Hkv,
                                                           int G, int L, int S, int Ns, int Nb, int n_rt,
                                                           int nbg, float c, int rr_step, int rr_shift,
                                                           int causal) {
   constexpr int KC = D / 16;
-  const int lane = threadIdx.x;
+  constexpr int PITCH = D * 2 + 16;      // LDS bytes per aggregated-key row
+  constexpr int RC = D / 8;              // 16-byte chunks per row
+  constexpr int CPT = 32 * RC / (kBsWaves * 64);  // chunks each thread stages per tile
+  static_assert(32 * RC % (kBsWaves * 64) == 0, "staging split");
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][32 * PITCH];
+
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
   int wg = blockIdx.x;
   const int rt = wg % n_rt;
   wg /= n_rt;
-  const int bg = wg % nbg;          // b * Hkv + g
-  const int I = Nb - 1 - wg / nbg;  // longest rows first
+  const int bg = wg % nbg;                        // b * Hkv + g
+  const int I0 = Nb - 1 - (wg / nbg) * kBsWaves;  // longest rows first
+  const int I = I0 - wv;                          // this wave's query block (< 0: idle)
+  const bool active = I >= 0;
   const int b = bg / Hkv;
   const int g = bg % Hkv;
 
   const int rho = rt * 32 + col;    // sampled-query slot inside the group
-  const bool valid = rho < G * R;
+  const bool valid = active && rho < G * R;
   const int hh = valid ? rho / R : 0;
   const int ii = rho % R;
   const int h = g * G + hh;
@@ -94,37 +103,98 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
       qb[kc] = as_bf16x8(w);
     }
   }
-  const uint16_t* kbase = kagg + static_cast<int64_t>(bg) * Ns * D + half * 8;
+  const uint16_t* kbase = kagg + static_cast<int64_t>(bg) * Ns * D;
   const int nvis = causal ? (I + 1) * R : Nb * R;  // strides of the candidate blocks
-  const int ntile = (nvis + 31) / 32;
+  const int ntile = active ? (nvis + 31) / 32 : 0;
+  const int ntile_wg = ((causal ? (I0 + 1) * R : Nb * R) + 31) / 32;  // wave 0's, the most
   const int jmax = has_q ? (causal ? i : Ns - 1) : -1;  // visible strides: j <= i (all when not causal)
+  // Tiles wholly at or below the smallest visible stride of the wave need no
+  // mask (lanes without a query hold Q = 0, so their scores are 0 and finite).
+  int jlim = has_q ? jmax : INT_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) jlim = min(jlim, __shfl_xor(jlim, o, 64));
+  jlim = __builtin_amdgcn_readfirstlane(jlim);
 
-  // ---- pass 1: row max and denominator (base-2 logits) ----
-  float m = -INFINITY, z = 0.0f;
-  u32x4 a_cur[KC], a_nxt[KC];
-  load_kagg_tile<D>(a_cur, kbase, min(col, Ns - 1));
-  for (int jt = 0; jt < ntile; ++jt) {
-    if (jt + 1 < ntile) load_kagg_tile<D>(a_nxt, kbase, min((jt + 1) * 32 + col, Ns - 1));
-    const floatx16 acc = tile_mma<D>(a_cur, qb);
-    float x[16];
-    float tm = -INFINITY;
+  // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1).
+  auto load_regs = [&](int jt, u32x4 (&r)[CPT]) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int ch = tid + e * kBsWaves * 64;
+      const int64_t jrow = min(jt * 32 + ch / RC, Ns - 1);
+      r[e] = *reinterpret_cast<const u32x4*>(kbase + jrow * D + (ch % RC) * 8);
+    }
+  };
+  auto store_lds = [&](int buf, const u32x4 (&r)[CPT]) {
+#pragma unroll
+    for (int e = 0; e < CPT; ++e) {
+      const int ch = tid + e * kBsWaves * 64;
+      *reinterpret_cast<u32x4*>(&kt[buf][(ch / RC) * PITCH + (ch % RC) * 16]) = r[e];
+    }
+  };
+  auto frag = [&](int buf, u32x4 (&a)[KC]) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(&kt[buf][col * PITCH + (2 * kc + half) * 16]);
+  };
+  // Runs f(jt, A fragments) over the wave's tiles; every wave takes part in the
+  // staging and the barriers of all ntile_wg tiles.  Buffer jt & 1 is refilled
+  // only after the barrier that follows its last reads.
+  auto over_tiles = [&](auto&& f) {
+    u32x4 r[CPT];
+    load_regs(0, r);
+    store_lds(0, r);
+    __syncthreads();
+    for (int jt = 0; jt < ntile_wg; ++jt) {
+      const int buf = jt & 1;
+      if (jt + 1 < ntile_wg) load_regs(jt + 1, r);
+      if (jt < ntile) {
+        u32x4 a[KC];
+        frag(buf, a);
+        f(jt, a);
+      }
+      if (jt + 1 < ntile_wg) store_lds(buf ^ 1, r);
+      __syncthreads();
+    }
+  };
+  // Masked base-2 logits of tile jt (only the tiles that reach past jlim).
+  auto masked = [&](int jt, const floatx16& acc, float (&x)[16]) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int j = jt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
       x[v] = (j <= jmax) ? acc[v] * c : -INFINITY;
-      tm = fmaxf(tm, x[v]);
     }
-    if (tm > -INFINITY) {
-      const float mn = fmaxf(m, tm);
+  };
+
+  // ---- pass 1: row max and denominator (base-2 logits) ----
+  float m = -INFINITY, z = 0.0f;
+  auto pass1 = [&](int jt, const u32x4 (&a)[KC]) {
+    const floatx16 acc = tile_mma<D>(a, qb);
+    if (jt * 32 + 31 <= jlim) {
+      float tm = acc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) tm = fmaxf(tm, acc[v]);
+      const float mn = fmaxf(m, tm * c);
       float zz = z * fast_exp2(m - mn);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) zz += fast_exp2(x[v] - mn);
+      for (int v = 0; v < 16; ++v) zz += fast_exp2(fmaf(acc[v], c, -mn));
       z = zz;
       m = mn;
-    }
+    } else {
+      float x[16];
+      masked(jt, acc, x);
+      float tm = -INFINITY;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) a_cur[kc] = a_nxt[kc];
-  }
+      for (int v = 0; v < 16; ++v) tm = fmaxf(tm, x[v]);
+      if (tm > -INFINITY) {
+        const float mn = fmaxf(m, tm);
+        float zz = z * fast_exp2(m - mn);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) zz += fast_exp2(x[v] - mn);
+        z = zz;
+        m = mn;
+      }
+    }
+  };
+  over_tiles(pass1);
   {
     const float mo = shfl_xor_f(m, 32);
     const float zo = shfl_xor_f(z, 32);
@@ -142,15 +212,17 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
   const int jlast = causal ? I : Nb - 1;  // last key block of the row
 
   // ---- pass 2: probabilities pooled into block cells ----
-  load_kagg_tile<D>(a_cur, kbase, min(col, Ns - 1));
-  for (int jt = 0; jt < ntile; ++jt) {
-    if (jt + 1 < ntile) load_kagg_tile<D>(a_nxt, kbase, min((jt + 1) * 32 + col, Ns - 1));
-    const floatx16 acc = tile_mma<D>(a_cur, qb);
-    float p[16];
+  auto pass2 = [&](int jt, const u32x4 (&a)[KC]) {
+    const floatx16 acc = tile_mma<D>(a, qb);
+    float e[16];  // unnormalised probabilities; 1/z is applied to the in-lane sums
+    if (jt * 32 + 31 <= jlim) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int j = jt * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      p[v] = (j <= jmax) ? fast_exp2(acc[v] * c - m) * invz : 0.0f;
+      for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -m));
+    } else {
+      float x[16];
+      masked(jt, acc, x);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) e[v] = (x[v] > -INFINITY) ? fast_exp2(x[v] - m) : 0.0f;
     }
     if constexpr (R >= 8) {
       // A block spans R >= 8 strides: groups of 4 values (v >> 2) in both lane halves.
@@ -159,14 +231,9 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
 #pragma unroll
       for (int u = 0; u < NJ; ++u) part[u] = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[(8 * (v >> 2)) / R] += p[v];
+      for (int v = 0; v < 16; ++v) part[(8 * (v >> 2)) / R] += e[v];
 #pragma unroll
-      for (int u = 0; u < NJ; ++u) {
-        float t = part[u] + shfl_xor_f(part[u], 32);
-#pragma unroll
-        for (int off = 1; off < R; off <<= 1) t += shfl_xor_f(t, off);
-        part[u] = t;
-      }
+      for (int u = 0; u < NJ; ++u) part[u] = group_sum<R>(sum_halves(part[u] * invz));
       if (valid && half == 0 && (col % R) == 0) {
 #pragma unroll
         for (int u = 0; u < NJ; ++u) {
@@ -182,14 +249,9 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
 #pragma unroll
       for (int u = 0; u < NJL; ++u) part[u] = 0.0f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[(v >> 2) * PER + (v & 3) / R] += p[v];
+      for (int v = 0; v < 16; ++v) part[(v >> 2) * PER + (v & 3) / R] += e[v];
 #pragma unroll
-      for (int u = 0; u < NJL; ++u) {
-        float t = part[u];
-#pragma unroll
-        for (int off = 1; off < R; off <<= 1) t += shfl_xor_f(t, off);
-        part[u] = t;
-      }
+      for (int u = 0; u < NJL; ++u) part[u] = group_sum<R>(part[u] * invz);
       if (valid && (col % R) == 0) {
 #pragma unroll
         for (int u = 0; u < NJL; ++u) {
@@ -199,12 +261,11 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const uint16_t* __rest
         }
       }
     }
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) a_cur[kc] = a_nxt[kc];
-  }
+  };
+  over_tiles(pass2);
 
   // ---- zeros above the diagonal for the heads of this row tile ----
-  if (!causal) return;
+  if (!causal || !active) return;
   constexpr int HPT = 32 / R;  // heads per row tile
   for (int t = 0; t < HPT; ++t) {
     const int hz = rt * HPT + t;
@@ -218,9 +279,10 @@ template <int D, int R>
 static void launch_bs(const Shape& s, const uint16_t* q, const uint16_t* kagg, float* score, hipStream_t st) {
   const int n_rt = (s.G * R + 31) / 32;
   const int nbg = s.Bz * s.Hkv;
-  const int64_t blocks = static_cast<int64_t>(n_rt) * nbg * s.Nb;
+  const int64_t blocks = static_cast<int64_t>(n_rt) * nbg * ((s.Nb + kBsWaves - 1) / kBsWaves);
   const float c = s.scale * kLog2e;
-  hipLaunchKernelGGL((block_scores_kernel<D, R>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, st, q, kagg,
+  hipLaunchKernelGGL((block_scores_kernel<D, R>), dim3(static_cast<unsigned>(blocks)), dim3(kBsWaves * 64), 0, st,
+                     q, kagg,
                      score, s.H, s.Hkv, s.G, s.L, s.S, s.Ns, s.Nb, n_rt, nbg, c, s.rr_step,
                      s.rr_shift, s.causal ? 1 : 0);
 }

@@ -58,6 +58,38 @@ __device__ __forceinline__ float sum_halves(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// v[lane] + v[lane ^ 16] on every lane (v_permlane16_swap: odd and even 16-lane rows).
+__device__ __forceinline__ float sum_rows16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Lane permutations inside 16-lane rows (DPP controls).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15 - i
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i (in each half row)
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum of v over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
+// in every lane of the group.  The mirrors pair lane i with its reflection, so
+// after them each pair sum sits in the first half of the group and the quad
+// steps finish it.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32, "group size");
+  if constexpr (N == 32) v = sum_rows16(v);
+  if constexpr (N >= 16) v += dpp<kDppRowMirror>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppXor2>(v);
+  return v;
+}
+
 }  // namespace rra
 
 #endif  // RRA_DEVICE_H_

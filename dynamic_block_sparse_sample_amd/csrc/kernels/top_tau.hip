@@ -63,14 +63,17 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(~static_cast<uint32_t>(key >> 32));
 }
 
+// NMAX: largest row length the LDS arrays hold (a power of two >= Nb), so rows
+// of short sequences do not pay the LDS, and the occupancy, of 4096 blocks.
+template <int NMAX>
 __global__ __launch_bounds__(kTopThreads) void top_tau_kernel(const float* __restrict__ score,
                                                               uint8_t* __restrict__ mask,
                                                               int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ cnt, int Nb,
                                                               double tau, int protect_last, int keep_all,
                                                               int causal) {
-  __shared__ uint64_t keys[kMaxBlocks];
-  __shared__ int flags[kMaxBlocks];
+  __shared__ uint64_t keys[NMAX];
+  __shared__ int flags[NMAX];
   __shared__ double dsh[kTopWaves];
   __shared__ int ish[kTopWaves];
 
@@ -165,9 +168,19 @@ int launch_top_tau(const Shape& s, float tau, int protect_last, const float* sco
   const int64_t rows = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
   if (rows == 0) return 0;
   const int keep_all = tau >= 1.0f ? 1 : 0;
-  hipLaunchKernelGGL(top_tau_kernel, dim3(static_cast<unsigned>(rows)), dim3(kTopThreads), 0,
-                     static_cast<hipStream_t>(stream), score, mask, idx, cnt, s.Nb, static_cast<double>(tau),
-                     protect_last, keep_all, s.causal ? 1 : 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<unsigned>(rows));
+  const int causal = s.causal ? 1 : 0;
+  const double t = static_cast<double>(tau);
+  if (s.Nb <= 256)
+    hipLaunchKernelGGL(top_tau_kernel<256>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
+                       protect_last, keep_all, causal);
+  else if (s.Nb <= 1024)
+    hipLaunchKernelGGL(top_tau_kernel<1024>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
+                       protect_last, keep_all, causal);
+  else
+    hipLaunchKernelGGL(top_tau_kernel<kMaxBlocks>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
+                       protect_last, keep_all, causal);
   return static_cast<int>(hipGetLastError());
 }
 
