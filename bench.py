@@ -96,14 +96,15 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "profile", "power", "selection"], default="bench",
+    ap.add_argument("--mode", choices=["bench", "profile", "power", "selection", "workloads"], default="bench",
                     help="profile: one estimate, --steps sparse-attention launches, one dense launch and a "
                          "256 MiB device copy (HBM-counter calibration); prints a short summary only. "
                          "power: socket power (amd-smi) while sparse attention, dense attention and the "
                          "MFMA probe each run back to back for --power-secs seconds. "
                          "selection: precision / recall / F1 and kept attention mass of the estimated "
                          "selections (round-robin variants, several S and tau) against the exact Top-tau "
-                         "selection, one JSON line per point")
+                         "selection, one JSON line per point. workloads: estimate / sparse / dense times and "
+                         "density of every bf16 workload at its own settings, one JSON line each")
     ap.add_argument("--power-secs", type=float, default=6.0)
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic_sparse_attn_llama_128k.json"))
@@ -124,6 +125,10 @@ def main(argv=None) -> int:
         return 1
     if args.mode == "selection":
         for line in selection_report(args.workload):
+            print(json.dumps(line), flush=True)
+        return 0
+    if args.mode == "workloads":
+        for line in workloads_report():
             print(json.dumps(line), flush=True)
         return 0
     w = wl.WORKLOADS[args.workload]
@@ -273,6 +278,12 @@ def main(argv=None) -> int:
         "mask_density": round(density, 5),
         "estimator_kernels_ms": {kk: round(vv, 4) for kk, vv in brk.items()},
         "estimator_hbm_frac": round(est_bytes / (t_est * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        # max(bytes / BW, executed flops / P_bf16) / t: the two-pass scores execute
+        # 2 * 2d * Bz * H * Ns (Ns + 1) / 2 flops (the exps bind less on this part)
+        "estimator_binding_roofline_frac": round(
+            max(est_bytes / (PEAK_HBM_GBS * 1e9),
+                2 * 2.0 * d * w.batch * w.num_heads * ns * (ns + 1) / 2 / (PEAK_BF16_TFLOPS * 1e12))
+            / (t_est * 1e-3), 4),
         "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (brk["stride_aggregate"] * 1e-3) / 1e9
                                            / PEAK_HBM_GBS, 4),
         "dense_attn_tflops": round(f_dense / (t_dense * 1e-3) / 1e12, 2),
@@ -335,6 +346,52 @@ SELECTION_POINTS = {
     "video_64k": [(16, 0.95)],
     "llama_128k": [(16, 0.9)],
 }
+
+
+def workloads_report(reps=5):
+    """Estimator, sparse and dense attention times of every bf16 workload."""
+    import torch
+
+    import dynamic_block_sparse_sample_amd as rra
+    from dynamic_block_sparse_sample_amd import workloads as wl
+
+    for name, w in wl.WORKLOADS.items():
+        if w.fp32_inputs:
+            continue
+        log(f"[workloads] {name}")
+        q, k, v = wl.make_inputs(w)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        del q, k, v
+        p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block, w.tau)
+        ws = rra.alloc_workspace(p, qd.device)
+        sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
+        out = torch.empty_like(qd)
+        times = {}
+        for tag, fn in (("estimate", lambda: rra.estimate(p, qd, kd, workspace=ws, out=sel)),
+                        ("sparse_attn", lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)),
+                        ("dense_attn", lambda: rra.dense_attn(p, qd, kd, vd, out=out))):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times[tag] = a.elapsed_time(b) / reps
+        nb = p.num_blocks
+        sum_cnt = int(sel.cnt.sum())
+        f_sel = 4.0 * w.head_dim * w.block * w.block * sum_cnt
+        f_full = 4.0 * w.head_dim * w.block * w.block * w.batch * w.num_heads * nb * (nb + 1) / 2
+        yield {"mode": "workloads", "workload": name, "seq_len": w.seq_len, "heads": f"{w.num_heads}/{w.num_kv_heads}",
+               "stride": w.stride, "tau": w.tau, "density": round(sum_cnt / (w.batch * w.num_heads * nb * (nb + 1) / 2), 4),
+               "t_estimate_ms": round(times["estimate"], 4), "t_sparse_attn_ms": round(times["sparse_attn"], 4),
+               "t_dense_attn_ms": round(times["dense_attn"], 4),
+               "sparse_tflops": round(f_sel / (times["sparse_attn"] * 1e-3) / 1e12, 1),
+               "dense_tflops": round(f_full / (times["dense_attn"] * 1e-3) / 1e12, 1),
+               "speedup_vs_dense": round(times["dense_attn"] / (times["estimate"] + times["sparse_attn"]), 3)}
+        del qd, kd, vd, out, ws, sel
+        torch.cuda.empty_cache()
 
 
 def xattn_supported(p) -> bool:
