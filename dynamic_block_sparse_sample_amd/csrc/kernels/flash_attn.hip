@@ -30,7 +30,8 @@
 //                  are enumerated in the order the first product left them.
 // The 16 MFMAs of S(s+1) are issued in chunks, each followed by one pair of
 // probabilities of S(s) and the LDS read of a K fragment four MFMAs ahead;
-// sched_barrier keeps that order so MFMA and VALU work overlap in one wave.
+// sched_barrier keeps that order so MFMA and VALU work overlap in one wave,
+// and the wave raises its issue priority (s_setprio) for that stream.
 // The running max is exact (the largest probability of a row is exactly 1, so
 // the dominant term of a peaked row carries no bf16 rounding); O and l are
 // rescaled only on sub-tiles where some row's max increased.
@@ -401,6 +402,9 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
     };
 #pragma unroll
     for (int i = 0; i < AHEAD; ++i) kf[i] = kfrag(i);
+    // Higher issue priority for the interleaved MFMA / softmax stream than for
+    // the other wave's P V burst on this SIMD (measured: 2 % faster sparse).
+    __builtin_amdgcn_s_setprio(2);
     u32x4 pb[2][2];
     float lsum = 0.0f;
     constexpr int NCHUNK = NM > 16 ? NM : 16;  // 16 probability pairs per sub-tile
@@ -417,6 +421,7 @@ __global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     // Keep the probabilities in this block (ahead of the rescale branch).
 #pragma unroll
     for (int t = 0; t < 2; ++t)
