@@ -1,6 +1,7 @@
-// Block-sparse causal flash attention for prefill (RRAttention §4.1: attention
+// Block-sparse flash attention for prefill (RRAttention §4.1: attention
 // computed only on the selected key blocks; dense FlashAttention is the same
-// kernel with every causal block listed).
+// kernel with every causal block listed).  Causal by default; without the
+// causal mask for encoder-style use.
 //
 // One workgroup per (batch, query head h, query block I) with BLK/32 waves;
 // wave w owns 32 queries.  Key blocks are consumed in 64-key sub-tiles.
@@ -43,9 +44,10 @@
 // sequence are masked.
 //
 // Work order: KV groups in phases small enough for the memory-side cache;
-// inside a phase longest rows (largest I) first, each group's workgroups on a
-// fixed set of XCDs (workgroup w runs on XCD w mod 8), the heads of a group
-// adjacent so that they stream the same K/V through one L2.
+// inside a phase longest rows (largest I) first (workgroup w runs on XCD
+// w mod 8), the heads of a group adjacent so that they stream the same K/V
+// through one L2, the group served by an XCD rotating every 16 slots so that
+// denser groups do not leave other XCDs idle.
 #include <cmath>
 #include <type_traits>
 #include <utility>
