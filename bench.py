@@ -85,7 +85,18 @@ def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=4, n_rows_sa
                    f"(head, query-block) rows ({blocks_sample} key blocks); extrapolated to the whole layer "
                    f"by heads and by selected blocks: {t_total:.0f} s per step"),
         "extrapolated_s_per_step": t_total,
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main(argv=None) -> int:
@@ -198,7 +209,8 @@ def main(argv=None) -> int:
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    t_sp = sum(a.elapsed_time(b) for a, b in sp_ev) / args.steps
+    sp_times = sorted(a.elapsed_time(b) for a, b in sp_ev)
+    t_sp = sum(sp_times) / args.steps
     t_est = sum(a.elapsed_time(b) for a, b in est_ev) / args.steps
 
     # per-kernel breakdown of the estimator (same buffers)
@@ -235,6 +247,11 @@ def main(argv=None) -> int:
     sum_cnt = int(cnt.sum())
     causal_blocks = p.batch * p.num_heads * nb * (nb + 1) // 2
     density = sum_cnt / causal_blocks
+    # per head (SURVEY-style report: min / median / max), and without the protected last row
+    per_head = (cnt.double().sum(-1) / (nb * (nb + 1) / 2)).flatten().sort().values
+    dens_no_last = (sum_cnt - int(cnt[..., -1].sum())) / (p.batch * p.num_heads * nb * (nb - 1) / 2) if nb > 1 else 1.0
+    # exact unmasked work: a selected diagonal block has Bk (Bk + 1) / 2 causal (t, u) pairs, not Bk^2
+    diag_sel = int(torch.diagonal(sel.mask, dim1=-2, dim2=-1).long().sum())
     L, d, Bk = w.seq_len, w.head_dim, w.block
     f_dense = 4.0 * d * w.batch * w.num_heads * L * (L + 1) / 2
     f_sel = 4.0 * d * Bk * Bk * sum_cnt
@@ -276,6 +293,13 @@ def main(argv=None) -> int:
         "t_dense_attn_ms": round(t_dense, 4),
         "speedup_vs_dense": round(t_dense / ms_step, 4),
         "mask_density": round(density, 5),
+        "mask_density_per_head": {"min": round(float(per_head[0]), 5),
+                                  "median": round(float(per_head[len(per_head) // 2]), 5),
+                                  "max": round(float(per_head[-1]), 5)},
+        "mask_density_without_protected_row": round(dens_no_last, 5),
+        "t_sparse_attn_ms_median_min": [round(sp_times[len(sp_times) // 2], 4), round(sp_times[0], 4)],
+        "sparse_attn_unmasked_tflops": round(
+            (f_sel - 4.0 * d * diag_sel * (Bk * Bk - Bk * (Bk + 1) / 2)) / (t_sp * 1e-3) / 1e12, 2),
         "estimator_kernels_ms": {kk: round(vv, 4) for kk, vv in brk.items()},
         "estimator_hbm_frac": round(est_bytes / (t_est * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         # max(bytes / BW, executed flops / P_bf16) / t: the two-pass scores execute
