@@ -37,7 +37,8 @@ def _head_scores(q, k, prm, h):
     """Oracle block scores of one query head: [Nb, Nb]."""
     g = h // prm.group
     kagg = orc.aggregate_keys(k[0, g].double().numpy(), prm.stride)
-    s = orc.stride_scores(q[0, h].double().numpy(), kagg, prm.stride, h, prm.scale)
+    s = orc.stride_scores(q[0, h].double().numpy(), kagg, prm.stride, h, prm.scale, prm.rr_mode, prm.rr_layer,
+                          prm.rr_fixed, prm.causal)
     return orc.pool_blocks(orc.stride_softmax(s), prm.strides_per_block)
 
 
@@ -186,3 +187,50 @@ def test_max_blocks_4096():
     err = check_output_rows(out, q.double().numpy(), k.double().numpy(), v.double().numpy(),
                             sel.mask.cpu().numpy(), prm, [(0, 0, 4095), (0, 0, 2048)])
     assert err <= OUT_ATOL
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_32k_sampled(causal):
+    """L = 32768 + 77 (last block of 77 tokens, plain work order), sampled mask
+    rows and output rows against the oracle."""
+    L, H, Hkv, d, S, Bk, tau = 32768 + 77, 8, 2, 128, 16, 128, 0.9
+    q, k, v = wl.make_random(1, H, Hkv, L, d, seed=11, scale=1.2, diag=1.0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    p = rra.make_params(1, H, Hkv, L, d, S, Bk, tau, causal=causal)
+    prm = orc.Params(1, H, Hkv, L, d, S, Bk, float(np.float32(tau)), True, causal=causal)
+    sel = rra.estimate(p, qd, kd, return_score=True)
+    out = rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt)
+    torch.cuda.synchronize()
+    near = _mask_parity(sel, q, k, prm, heads=[0, 5])
+    nb = p.num_blocks
+    rows = [(0, 0, nb - 1), (0, 5, nb - 1), (0, 3, nb // 2), (0, 7, 0)]
+    err = check_output_rows(out, q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                            sel.mask.cpu().numpy(), prm, rows)
+    say(f"ragged 32K+77 causal={causal}: near-tie rows {near}, sampled output err {err:.2e}")
+    assert err <= OUT_ATOL
+
+
+def test_concurrent_streams_match_sequential():
+    """The library keeps no mutable global state: the same calls on two streams
+    at once give bitwise the results of running them one after the other."""
+    w = wl.WORKLOADS["llama_8k"]
+    q, k, v = wl.make_inputs(w)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    p1 = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, 16, w.block, 0.9)
+    p2 = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, 8, w.block, 0.8)
+    ref = []
+    for p in (p1, p2):
+        sel = rra.estimate(p, qd, kd)
+        ref.append((sel.mask.clone(), rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt).clone()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    got = [None, None]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for j, (p, s) in enumerate(zip((p1, p2), streams)):
+            with torch.cuda.stream(s):
+                sel = rra.estimate(p, qd, kd)
+                got[j] = (sel.mask, rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt))
+        torch.cuda.synchronize()
+        for j in range(2):
+            assert torch.equal(got[j][0], ref[j][0]) and torch.equal(got[j][1], ref[j][1]), (rep, j)
