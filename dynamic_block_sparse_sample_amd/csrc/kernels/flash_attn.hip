@@ -146,8 +146,10 @@ __device__ __forceinline__ void lds_reads_done_barrier() {
 
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
+// Two workgroups per CU (64 KB of LDS each): two waves per SIMD for BLK = 128,
+// one for BLK = 64 (two waves per workgroup).
 template <int D, int BLK>
-__global__ __launch_bounds__((BLK / 32) * 64, 2) void flash_attn_kernel(
+__global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
     int Hkv, int G, int L, int Nb, float c, int gp, int causal) {
