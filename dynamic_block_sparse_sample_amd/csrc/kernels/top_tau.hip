@@ -2,165 +2,201 @@
 // block protection of §4.3; the same minimal-cumulative-set rule as
 // XAttention's threshold selection).
 //
-// One 256-thread workgroup per row (b, h, I).  The candidates are the I+1
-// causal key blocks (every key block when not causal); a row with a zero total
-// (a last partial query block without a sampled query: no estimate) keeps them
-// all.  The candidates' block scores are
-// packed into 64-bit keys (inverted float bits << 32 | J), so one ascending
-// bitonic sort in LDS orders them by (score desc, J asc).  A float64 prefix
-// scan over the sorted scores finds k* = the first prefix reaching
-// tau * (row total); the k* selected blocks are flagged in LDS, written as the
-// mask row, and compacted in ascending J order by an exclusive scan into the
-// index list.
-#include <climits>
+// Per row (b, h, I) the candidates are the I+1 causal key blocks (every key
+// block when not causal).  In the order (score desc, J asc) the selection is
+// the shortest prefix whose sum reaches tau * T, T the row total; a row with
+// T = 0 (a last partial query block without a sampled query: no estimate)
+// keeps every candidate.
+//
+// No sort is needed.  One wave per row holds the row in registers (block J in
+// lane J mod 64, slot J / 64; a row runs with the fewest slots, a power of
+// two, that hold its candidates).  Scores are non-negative, so their float bit
+// patterns order like the values; the threshold value t is found by a
+// bitwise search over those 31 bits: t = the largest x with
+// sum(scores >= x) >= tau * T (float64 sums, one wave reduction per bit).
+// Every block scoring above t is then selected (their sum is below tau * T),
+// and of the blocks equal to t the m lowest J, m the smallest count with
+// sum(above) + m * t >= tau * T: exactly the prefix of the sorted order.
+// Ranks among equal scores and the ascending compaction of the selected J
+// come from per-slot ballots (a popcount of the lanes below).
+#include <cmath>
+#include <utility>
 
 #include "../rra_internal.h"
 #include "rra_device.h"
 
 namespace rra {
 
-constexpr int kTopThreads = 256;
-constexpr int kTopWaves = kTopThreads / 64;
+constexpr int kTopWaves = 4;  // rows per 256-thread workgroup
 
-template <typename T>
-__device__ __forceinline__ T block_exclusive_scan(T v, T* sh, T& total) {
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  T incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const T y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(u & 0xffffffffu), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                                     static_cast<uint32_t>(lo)));
+}
+
+// Sum over the 64 lanes, the same value in every lane: each step adds a
+// lane's value and its partner's, and the partner adds the same two numbers.
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppRowMirror>(v);
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto lo16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+  const auto hi16 =
+      __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+  v = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi16[0]) << 32) | lo16[0])) +
+      __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi16[1]) << 32) | lo16[1]));
+  const uint64_t w = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto lo32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w), static_cast<uint32_t>(w), false, false);
+  const auto hi32 =
+      __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi32[0]) << 32) | lo32[0])) +
+         __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi32[1]) << 32) | lo32[1]));
+}
+
+// f(integral_constant<k>) for k = 0 .. N-1, unrolled at compile time (the
+// per-slot arrays must stay in registers).
+template <typename F, int... K>
+__device__ __forceinline__ void for_slots_impl(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void for_slots(F&& f) {
+  for_slots_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lanes below this one among the set bits of a ballot.
+__device__ __forceinline__ int lanes_below(uint64_t ballot) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(ballot), 0));
+}
+
+// Rows of one slot-count class: NS slots in registers (NS * 64 >= candidates;
+// slots past the candidates hold zeros, which no threshold x >= 1 counts).
+template <int NS>
+__device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint8_t* __restrict__ mrow,
+                                            int32_t* __restrict__ irow, int32_t* __restrict__ cnt_out, int lane,
+                                            int n, int Nb, double tau) {
+  constexpr bool kKeepD = NS <= 16;
+  uint32_t bits[NS];
+  double val[kKeepD ? NS : 1];
+  auto value = [&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if constexpr (kKeepD) return val[k];
+    else return static_cast<double>(__uint_as_float(bits[k]));
+  };
+  double total = 0.0;
+  for_slots<NS>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const int J = k * 64 + lane;
+    const float v = J < n ? srow[J] : 0.0f;
+    bits[k] = v > 0.0f ? __float_as_uint(v) : 0u;  // zeros and non-candidates: 0
+    if constexpr (kKeepD) val[k] = v > 0.0f ? static_cast<double>(v) : 0.0;
+    total += value(kc);
+  });
+  total = wave_sum_d(total);
+  if (!(total > 0.0)) {  // no estimate: every candidate (the same in every lane)
+    for (int J = lane; J < Nb; J += 64) {
+      mrow[J] = J < n ? 1 : 0;
+      if (J < n) irow[J] = J;
+    }
+    if (lane == 0) *cnt_out = n;
+    return;
   }
-  if (lane == 63) sh[w] = incl;
-  __syncthreads();
-  T base = 0, tot = 0;
-#pragma unroll
-  for (int k = 0; k < kTopWaves; ++k) {
-    if (k < w) base += sh[k];
-    tot += sh[k];
+
+  // Threshold bits: the largest x with sum(bits >= x) >= tau * T (x >= 1,
+  // since the positive scores sum to T >= tau * T).
+  const double thr = tau * total;
+  uint32_t x = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = x | (1u << bit);
+    double s = 0.0;
+    for_slots<NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      s += bits[k] >= cand ? value(kc) : 0.0;
+    });
+    s = wave_sum_d(s);
+    if (__builtin_amdgcn_readfirstlane(s >= thr ? 1 : 0)) x = cand;
   }
-  __syncthreads();
-  total = tot;
-  return base + incl - v;
+
+  // Blocks above t, and the number of blocks equal to t.
+  double above = 0.0;
+  int n_eq = 0;
+  for_slots<NS>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    above += bits[k] > x ? value(kc) : 0.0;
+    n_eq += __popcll(__ballot(bits[k] == x));
+  });
+  above = wave_sum_d(above);
+  const double t = static_cast<double>(__uint_as_float(x));
+  // m: the fewest blocks equal to t that bring the sum to tau * T (1 <= m <= n_eq).
+  int m = 1;
+  {
+    const double need = (thr - above) / t;
+    if (need > 1.0) m = need < static_cast<double>(n_eq) ? static_cast<int>(ceil(need)) : n_eq;
+    while (m > 1 && above + static_cast<double>(m - 1) * t >= thr) --m;
+    while (m < n_eq && above + static_cast<double>(m) * t < thr) ++m;
+  }
+  m = __builtin_amdgcn_readfirstlane(m);
+
+  // Mask row, and the selected J compacted in ascending order.
+  int eq_before = 0, sel_before = 0;
+  for_slots<NS>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
+    const int J = k * 64 + lane;
+    const bool eq = bits[k] == x;
+    const uint64_t be = __ballot(eq);
+    const bool sel = bits[k] > x || (eq && eq_before + lanes_below(be) < m);
+    eq_before += __popcll(be);
+    if (J < Nb) mrow[J] = sel ? 1 : 0;
+    const uint64_t bs = __ballot(sel);
+    if (sel) irow[sel_before + lanes_below(bs)] = J;
+    sel_before += __popcll(bs);
+  });
+  for (int J = NS * 64 + lane; J < Nb; J += 64) mrow[J] = 0;  // beyond the candidates' slots
+  if (lane == 0) *cnt_out = sel_before;
 }
 
-__device__ __forceinline__ int block_min_int(int v, int* sh) {
+// SLOTS: 64-block slots the largest row needs (Nb <= 64 * SLOTS).
+template <int SLOTS>
+__global__ __launch_bounds__(64 * kTopWaves) void top_tau_kernel(const float* __restrict__ score,
+                                                                 uint8_t* __restrict__ mask,
+                                                                 int32_t* __restrict__ idx,
+                                                                 int32_t* __restrict__ cnt, int64_t rows, int Nb,
+                                                                 double tau, int protect_last, int keep_all,
+                                                                 int causal) {
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, 64));
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  int r = sh[0];
-#pragma unroll
-  for (int k = 1; k < kTopWaves; ++k) r = min(r, sh[k]);
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ float key_value(uint64_t key) {
-  return __uint_as_float(~static_cast<uint32_t>(key >> 32));
-}
-
-// NMAX: largest row length the LDS arrays hold (a power of two >= Nb), so rows
-// of short sequences do not pay the LDS, and the occupancy, of 4096 blocks.
-template <int NMAX>
-__global__ __launch_bounds__(kTopThreads) void top_tau_kernel(const float* __restrict__ score,
-                                                              uint8_t* __restrict__ mask,
-                                                              int32_t* __restrict__ idx,
-                                                              int32_t* __restrict__ cnt, int Nb,
-                                                              double tau, int protect_last, int keep_all,
-                                                              int causal) {
-  __shared__ uint64_t keys[NMAX];
-  __shared__ int flags[NMAX];
-  __shared__ double dsh[kTopWaves];
-  __shared__ int ish[kTopWaves];
-
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));  // uniform: scalar row
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kTopWaves + wv;
+  if (row >= rows) return;  // whole waves; no workgroup barrier below
   const int I = static_cast<int>(row % Nb);
   const int n = causal ? I + 1 : Nb;  // candidate key blocks
   const float* srow = score + row * Nb;
   uint8_t* mrow = mask + row * Nb;
   int32_t* irow = idx + row * Nb;
+  int32_t* crow = cnt + row;
 
   if (keep_all || (protect_last && I == Nb - 1) || n == 1) {
-    for (int J = tid; J < Nb; J += kTopThreads) {
+    for (int J = lane; J < Nb; J += 64) {
       mrow[J] = J < n ? 1 : 0;
       if (J < n) irow[J] = J;
     }
-    if (tid == 0) cnt[row] = n;
+    if (lane == 0) *crow = n;
     return;
   }
-
-  int np2 = 1;
-  while (np2 < n) np2 <<= 1;
-  for (int J = tid; J < np2; J += kTopThreads) {
-    uint64_t key = ~0ull;
-    if (J < n) key = (static_cast<uint64_t>(~__float_as_uint(srow[J])) << 32) | static_cast<uint32_t>(J);
-    keys[J] = key;
-  }
-  for (int J = tid; J < Nb; J += kTopThreads) flags[J] = 0;
-  __syncthreads();
-
-  // Bitonic sort, ascending.
-  for (int kk = 2; kk <= np2; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int t = tid; t < (np2 >> 1); t += kTopThreads) {
-        const int i0 = 2 * jj * (t / jj) + (t % jj);
-        const int i1 = i0 + jj;
-        const uint64_t a = keys[i0];
-        const uint64_t bkey = keys[i1];
-        const bool up = (i0 & kk) == 0;
-        if ((a > bkey) == up) {
-          keys[i0] = bkey;
-          keys[i1] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // Float64 prefix sums over the sorted scores.
-  const int per = (n + kTopThreads - 1) / kTopThreads;
-  const int p0 = tid * per;
-  double tsum = 0.0;
-  for (int e = 0; e < per; ++e) {
-    const int p = p0 + e;
-    if (p < n) tsum += static_cast<double>(key_value(keys[p]));
-  }
-  double total;
-  double c = block_exclusive_scan<double>(tsum, dsh, total);
-  const double thr = tau * total;
-  int first = INT_MAX;
-  for (int e = 0; e < per; ++e) {
-    const int p = p0 + e;
-    if (p < n) {
-      c += static_cast<double>(key_value(keys[p]));
-      if (c >= thr && first == INT_MAX) first = p;
-    }
-  }
-  const int fmin = block_min_int(first, ish);
-  const int kstar = (fmin == INT_MAX || !(total > 0.0)) ? n : fmin + 1;
-
-  for (int p = tid; p < kstar; p += kTopThreads) flags[static_cast<uint32_t>(keys[p])] = 1;
-  __syncthreads();
-  for (int J = tid; J < Nb; J += kTopThreads) mrow[J] = static_cast<uint8_t>(flags[J]);
-
-  // Ascending compaction of the selected J.
-  int fsum = 0;
-  for (int e = 0; e < per; ++e) {
-    const int J = p0 + e;
-    if (J < n) fsum += flags[J];
-  }
-  int ftotal;
-  int pos = block_exclusive_scan<int>(fsum, ish, ftotal);
-  for (int e = 0; e < per; ++e) {
-    const int J = p0 + e;
-    if (J < n && flags[J]) irow[pos++] = J;
-  }
-  if (tid == 0) cnt[row] = kstar;
+  const int ns = (n + 63) >> 6;  // slots holding candidates
+  if (ns <= 1) top_tau_row<1>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else if (SLOTS >= 2 && ns <= 2) top_tau_row<(SLOTS >= 2 ? 2 : 1)>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else if (SLOTS >= 4 && ns <= 4) top_tau_row<(SLOTS >= 4 ? 4 : 1)>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else if (SLOTS >= 8 && ns <= 8) top_tau_row<(SLOTS >= 8 ? 8 : 1)>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else if (SLOTS >= 16 && ns <= 16) top_tau_row<(SLOTS >= 16 ? 16 : 1)>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else if (SLOTS >= 32 && ns <= 32) top_tau_row<(SLOTS >= 32 ? 32 : 1)>(srow, mrow, irow, crow, lane, n, Nb, tau);
+  else top_tau_row<SLOTS>(srow, mrow, irow, crow, lane, n, Nb, tau);
 }
 
 int launch_top_tau(const Shape& s, float tau, int protect_last, const float* score, uint8_t* mask, int32_t* idx,
@@ -169,17 +205,18 @@ int launch_top_tau(const Shape& s, float tau, int protect_last, const float* sco
   if (rows == 0) return 0;
   const int keep_all = tau >= 1.0f ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>(rows));
+  const dim3 grid(static_cast<unsigned>((rows + kTopWaves - 1) / kTopWaves));
+  const dim3 block(64 * kTopWaves);
   const int causal = s.causal ? 1 : 0;
   const double t = static_cast<double>(tau);
   if (s.Nb <= 256)
-    hipLaunchKernelGGL(top_tau_kernel<256>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
-                       protect_last, keep_all, causal);
+    hipLaunchKernelGGL(top_tau_kernel<4>, grid, block, 0, st, score, mask, idx, cnt, rows, s.Nb, t, protect_last,
+                       keep_all, causal);
   else if (s.Nb <= 1024)
-    hipLaunchKernelGGL(top_tau_kernel<1024>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
-                       protect_last, keep_all, causal);
+    hipLaunchKernelGGL(top_tau_kernel<16>, grid, block, 0, st, score, mask, idx, cnt, rows, s.Nb, t, protect_last,
+                       keep_all, causal);
   else
-    hipLaunchKernelGGL(top_tau_kernel<kMaxBlocks>, grid, dim3(kTopThreads), 0, st, score, mask, idx, cnt, s.Nb, t,
+    hipLaunchKernelGGL(top_tau_kernel<kMaxBlocks / 64>, grid, block, 0, st, score, mask, idx, cnt, rows, s.Nb, t,
                        protect_last, keep_all, causal);
   return static_cast<int>(hipGetLastError());
 }
