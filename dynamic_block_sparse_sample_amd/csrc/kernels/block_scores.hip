@@ -135,24 +135,41 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(&kt[buf][col * PITCH + (2 * kc + half) * 16]);
   };
-  // Runs f(jt, A fragments) over the wave's tiles; every wave takes part in the
-  // staging and the barriers of all ntile_wg tiles.  Buffer jt & 1 is refilled
-  // only after the barrier that follows its last reads.
+  // Runs f(jt, S^T tile) over the wave's tiles, software-pipelined: the MFMAs
+  // of tile jt+1 are issued before f works on tile jt, so the MFMA unit and
+  // the VALU overlap inside the wave.  Every wave takes part in the staging
+  // and the barriers of all ntile_wg tiles.  Tiles jt and jt+1 sit in the two
+  // LDS buffers during step jt; tile jt+2 replaces tile jt at the end of the
+  // step, after the barrier that followed every wave's reads of tile jt.
   auto over_tiles = [&](auto&& f) {
     u32x4 r[CPT];
     load_regs(0, r);
     store_lds(0, r);
+    if (ntile_wg > 1) {
+      load_regs(1, r);
+      store_lds(1, r);
+    }
     __syncthreads();
+    floatx16 acc_cur, acc_next;
+    if (ntile > 0) {
+      u32x4 a[KC];
+      frag(0, a);
+      acc_cur = tile_mma<D>(a, qb);
+    }
+    __syncthreads();  // every wave has read tile 0 before step 0 refills its buffer
     for (int jt = 0; jt < ntile_wg; ++jt) {
       const int buf = jt & 1;
-      if (jt + 1 < ntile_wg) load_regs(jt + 1, r);
-      if (jt < ntile) {
+      const bool refill = jt + 2 < ntile_wg;
+      if (refill) load_regs(jt + 2, r);
+      if (jt + 1 < ntile) {
         u32x4 a[KC];
-        frag(buf, a);
-        f(jt, a);
+        frag(buf ^ 1, a);
+        acc_next = tile_mma<D>(a, qb);
       }
-      if (jt + 1 < ntile_wg) store_lds(buf ^ 1, r);
+      if (jt < ntile) f(jt, acc_cur);
+      if (refill) store_lds(buf, r);
       __syncthreads();
+      acc_cur = acc_next;
     }
   };
   // Masked base-2 logits of tile jt (only the tiles that reach past jlim).
@@ -166,8 +183,7 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
 
   // ---- pass 1: row max and denominator (base-2 logits) ----
   float m = -INFINITY, z = 0.0f;
-  auto pass1 = [&](int jt, const u32x4 (&a)[KC]) {
-    const floatx16 acc = tile_mma<D>(a, qb);
+  auto pass1 = [&](int jt, const floatx16& acc) {
     if (jt * 32 + 31 <= jlim) {
       float tm = acc[0];
 #pragma unroll
@@ -212,8 +228,7 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   const int jlast = causal ? I : Nb - 1;  // last key block of the row
 
   // ---- pass 2: probabilities pooled into block cells ----
-  auto pass2 = [&](int jt, const u32x4 (&a)[KC]) {
-    const floatx16 acc = tile_mma<D>(a, qb);
+  auto pass2 = [&](int jt, const floatx16& acc) {
     float e[16];  // unnormalised probabilities; 1/z is applied to the in-lane sums
     if (jt * 32 + 31 <= jlim) {
 #pragma unroll
