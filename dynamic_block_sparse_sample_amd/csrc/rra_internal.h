@@ -9,7 +9,7 @@
 
 namespace rra {
 
-// Largest number of blocks per row the selection kernel sorts in LDS.
+// Largest number of blocks per row (the selection kernel holds a row in registers).
 constexpr int kMaxBlocks = 4096;
 
 struct Shape {

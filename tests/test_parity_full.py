@@ -172,7 +172,7 @@ def test_llama_128k_headline_in_bench_configuration():
 
 
 def test_max_blocks_4096():
-    """Nb = 4096 key blocks (the largest row the selection sorts), one head, S = Bk."""
+    """Nb = 4096 key blocks (the longest row the selection holds), one head, S = Bk."""
     L, d, S, Bk = 4096 * 128, 128, 128, 128
     q, k, v = wl.make_random(1, 1, 1, L, d, seed=3, scale=1.5, diag=1.0)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
