@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     RRAError,
     Selection,
     alloc_workspace,
+    attn_workspace_size,
     block_mass,
     block_scores,
     cast_f32_to_bf16,
@@ -27,7 +28,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "LIB_PATH", "Params", "RRAError", "Selection", "alloc_workspace", "block_mass", "block_scores",
+    "LIB_PATH", "Params", "RRAError", "Selection", "alloc_workspace", "attn_workspace_size", "block_mass",
+    "block_scores",
     "cast_f32_to_bf16",
     "dense_attn", "estimate", "lib", "make_params", "sparse_attn", "status_str", "stride_aggregate",
     "top_tau", "validate", "workspace_size", "xattn_block_scores",

@@ -70,8 +70,9 @@ SIGNATURES = {
     "rra_estimate": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P]),
     "rra_block_mass": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_xattn_block_scores": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
-    "rra_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P]),
-    "rra_dense_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
+    "rra_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "rra_dense_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "rra_attn_workspace_size": (ctypes.c_int, [ctypes.POINTER(Params), ctypes.POINTER(ctypes.c_size_t)]),
 }
 
 _lib = None
@@ -274,7 +275,29 @@ def estimate(p: Params, q: torch.Tensor, k: torch.Tensor, workspace: torch.Tenso
     return out
 
 
-def sparse_attn(p: Params, q, k, v, idx, cnt, out=None, stream=None) -> torch.Tensor:
+def attn_workspace_size(p: Params) -> int:
+    n = ctypes.c_size_t(0)
+    _check("rra_attn_workspace_size", lib().rra_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _attn_workspace(p: Params, device, workspace, schedule: str):
+    """(pointer, bytes) of the schedule workspace: a fresh one per call unless given
+    (calls that may overlap need distinct ones); (None, 0) for schedule="static"."""
+    if schedule == "static":
+        return None, 0
+    if schedule != "dynamic":
+        raise ValueError(f"schedule must be 'dynamic' or 'static', not {schedule!r}")
+    if workspace is None:
+        workspace = torch.empty(attn_workspace_size(p), dtype=torch.uint8, device=device)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def sparse_attn(p: Params, q, k, v, idx, cnt, out=None, workspace=None, schedule="dynamic",
+                stream=None) -> torch.Tensor:
+    """Block-sparse attention on the selected key blocks.  schedule="dynamic" (a
+    per-call workspace unless one is given) balances the rows over the XCDs;
+    "static" runs one workgroup per row.  Both give bitwise the same output."""
     qs, kv, nb, _ = _shapes(p)
     _need(q, "q", torch.bfloat16, qs)
     _need(k, "k", torch.bfloat16, kv)
@@ -284,12 +307,13 @@ def sparse_attn(p: Params, q, k, v, idx, cnt, out=None, stream=None) -> torch.Te
     if out is None:
         out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, qs)
+    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule)
     _check("rra_sparse_attn", lib().rra_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
-                                                    _ptr(cnt), _ptr(out), _stream(stream)))
+                                                    _ptr(cnt), _ptr(out), ws, ws_bytes, _stream(stream)))
     return out
 
 
-def dense_attn(p: Params, q, k, v, out=None, stream=None) -> torch.Tensor:
+def dense_attn(p: Params, q, k, v, out=None, workspace=None, schedule="dynamic", stream=None) -> torch.Tensor:
     qs, kv, _, _ = _shapes(p)
     _need(q, "q", torch.bfloat16, qs)
     _need(k, "k", torch.bfloat16, kv)
@@ -297,6 +321,7 @@ def dense_attn(p: Params, q, k, v, out=None, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, qs)
-    _check("rra_dense_attn", lib().rra_dense_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                                  _stream(stream)))
+    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule)
+    _check("rra_dense_attn", lib().rra_dense_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ws,
+                                                  ws_bytes, _stream(stream)))
     return out

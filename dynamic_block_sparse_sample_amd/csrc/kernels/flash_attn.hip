@@ -3,8 +3,9 @@
 // kernel with every causal block listed).  Causal by default; without the
 // causal mask for encoder-style use.
 //
-// One workgroup per (batch, query head h, query block I) with BLK/32 waves;
-// wave w owns 32 queries.  Key blocks are consumed in 64-key sub-tiles.
+// One work item per (batch, query head h, query block I), run by a workgroup
+// of BLK/32 waves (see Schedule below); wave w owns 32 queries.  Key blocks
+// are consumed in 64-key sub-tiles.
 //
 // Data movement: K and V sub-tiles (64 keys x d, row-major) are copied from
 // global memory straight into LDS with global_load_lds_dwordx4 (lane l's 16
@@ -44,10 +45,20 @@
 // sequence are masked.
 //
 // Work order: KV groups in phases small enough for the memory-side cache;
-// inside a phase longest rows (largest I) first (workgroup w runs on XCD
-// w mod 8), the heads of a group adjacent so that they stream the same K/V
-// through one L2, the group served by an XCD rotating every 16 slots so that
-// denser groups do not leave other XCDs idle.
+// inside a phase longest rows (largest I) first (item w goes to XCD w mod 8),
+// the heads of a group adjacent so that they stream the same K/V through one
+// L2, the group served by an XCD rotating every 16 slots so that denser
+// groups do not leave other XCDs idle.
+//
+// Schedule: with a counter workspace the grid is the resident workgroups
+// (occupancy x CUs, workgroup w on XCD w mod 8); each takes items w = 8k + x
+// from its XCD's queue with an atomic counter and, when that queue is empty,
+// from the other XCDs' queues.  The XCDs run at different clocks under the
+// power limit (measured up to 5 % apart for the same work), and a static
+// split leaves the fast ones idle while the slow ones finish.  Without the
+// workspace every item is its own workgroup.  Each item is computed the same
+// way either way, so the outputs are bitwise identical.
+#include <atomic>
 #include <cmath>
 #include <type_traits>
 #include <utility>
@@ -152,7 +163,7 @@ template <int D, int BLK>
 __global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, uint16_t* __restrict__ out, int H,
-    int Hkv, int G, int L, int Nb, float c, int gp, int causal) {
+    int Hkv, int G, int L, int Nb, float c, int gp, int causal, int nbg, uint32_t* __restrict__ sched) {
   using C = FaCfg<D, BLK>;
   // K and V rings of two sub-tiles each (K(t) in kb[t & 1], V(t) in vb[t & 1]),
   // in distinct LDS objects so every access names its buffer statically.
@@ -161,7 +172,10 @@ __global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_att
   __shared__ __attribute__((aligned(1024))) uint8_t vb0[C::TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t vb1[C::TILE];
 
-  // ---- work item ----
+  __shared__ int s_item;
+
+  // ---- one work item: (b, h, I) from the item index w ----
+  auto run_item = [&](const int w) {
   // Workgroup w runs on XCD w mod 8.  The KV groups are processed in phases of
   // `gp` groups (their K and V fit the memory-side cache together); inside a
   // phase XCD x takes every (8/gp)-th query block, longest rows first, the
@@ -170,10 +184,8 @@ __global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_att
   // workgroups an XCD holds at once, so neighbouring query blocks of a group,
   // whose lists overlap, still share the L2): groups differ in density, and a
   // fixed assignment would leave the XCDs of the sparser groups idle at the end.
-  const int nbg = static_cast<int>(gridDim.x / (static_cast<unsigned>(G) * Nb));  // Bz * Hkv
   int bg, hh, I;
   {
-    const int w = blockIdx.x;
     if (gp > 0) {
       const int phase_items = gp * G * Nb;
       const int ph = w / phase_items;
@@ -493,6 +505,43 @@ __global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_att
       *reinterpret_cast<u32x2*>(orow + 32 * ct + 8 * g4 + 4 * half) = w;
     }
   }
+  };  // run_item
+
+  // ---- items: blockIdx.x alone, or popped from the XCD queues ----
+  const int n_items = nbg * G * Nb;
+  const int x0 = blockIdx.x % kSchedQueues;
+  int tries = 0;  // queues thread 0 has found empty, in the order x0, x0 + 1, ...
+  auto pop = [&]() -> int {
+    if (threadIdx.x == 0) {
+      int it = -1;
+      while (tries < kSchedQueues) {
+        const int x = (x0 + tries) % kSchedQueues;
+        const int n_x = (n_items - x + kSchedQueues - 1) / kSchedQueues;  // items w = 8k + x < n_items
+        const uint32_t kq = atomicAdd(&sched[kSchedStride * x], 1u);
+        if (kq < static_cast<uint32_t>(n_x)) {
+          it = kSchedQueues * static_cast<int>(kq) + x;
+          break;
+        }
+        ++tries;
+      }
+      s_item = it;
+    }
+    __syncthreads();
+    const int it = s_item;
+    __syncthreads();  // every thread has read s_item before thread 0 rewrites it
+    return it;
+  };
+  int item = (sched == nullptr) ? static_cast<int>(blockIdx.x) : pop();
+  while (item >= 0) {
+    run_item(item);
+    item = (sched == nullptr) ? -1 : pop();
+  }
+}
+
+// Clears the schedule counters (a kernel, not a memset, so the launch can be
+// captured in a graph).
+__global__ void sched_clear_kernel(uint32_t* __restrict__ sched) {
+  for (int i = threadIdx.x; i < kSchedQueues * kSchedStride; i += blockDim.x) sched[i] = 0u;
 }
 
 // Groups per phase of the work order: the largest gp in {8, 4, 2, 1} that
@@ -509,28 +558,57 @@ static int phase_groups(const Shape& s) {
   return s.Nb % 8 == 0 ? 1 : 0;  // one group per phase even above the budget
 }
 
+// Workgroups of flash_attn_kernel<D, BLK> resident at once on the current
+// device (occupancy x CUs), 0 if unknown; cached per device and kernel.
 template <int D, int BLK>
-static void launch_fa(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                      const int32_t* cnt, uint16_t* out, hipStream_t st) {
-  const int64_t blocks = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
-  hipLaunchKernelGGL((flash_attn_kernel<D, BLK>), dim3(static_cast<unsigned>(blocks)), dim3(FaCfg<D, BLK>::NT), 0,
+static int resident_workgroups() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, flash_attn_kernel<D, BLK>, FaCfg<D, BLK>::NT, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  n = per_cu * cus;
+  n -= n % kSchedQueues;  // whole rounds over the XCDs
+  if (n > 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D, int BLK>
+static int launch_fa(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
+                     const int32_t* cnt, uint16_t* out, uint32_t* sched, hipStream_t st) {
+  const int64_t items = static_cast<int64_t>(s.Bz) * s.H * s.Nb;
+  int64_t grid = items;
+  if (sched != nullptr) {
+    const int resident = resident_workgroups<D, BLK>();
+    if (resident > 0 && items > resident) {
+      hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(256), 0, st, sched);
+      const int err = static_cast<int>(hipGetLastError());
+      if (err != 0) return err;
+      grid = resident;
+    } else {
+      sched = nullptr;  // every item has a workgroup of its own anyway
+    }
+  }
+  hipLaunchKernelGGL((flash_attn_kernel<D, BLK>), dim3(static_cast<unsigned>(grid)), dim3(FaCfg<D, BLK>::NT), 0,
                      st, q, k, v, idx, cnt, out, s.H, s.Hkv, s.G, s.L, s.Nb, s.scale * kLog2e, phase_groups(s),
-                     s.causal ? 1 : 0);
+                     s.causal ? 1 : 0, s.Bz * s.Hkv, sched);
+  return static_cast<int>(hipGetLastError());
 }
 
 int launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* idx,
-                      const int32_t* cnt, uint16_t* out, void* stream) {
+                      const int32_t* cnt, uint16_t* out, uint32_t* sched, void* stream) {
   if (static_cast<int64_t>(s.Bz) * s.Nb == 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (s.d == 128 && s.Bk == 128)
-    launch_fa<128, 128>(s, q, k, v, idx, cnt, out, st);
-  else if (s.d == 128 && s.Bk == 64)
-    launch_fa<128, 64>(s, q, k, v, idx, cnt, out, st);
-  else if (s.d == 64 && s.Bk == 128)
-    launch_fa<64, 128>(s, q, k, v, idx, cnt, out, st);
-  else
-    launch_fa<64, 64>(s, q, k, v, idx, cnt, out, st);
-  return static_cast<int>(hipGetLastError());
+  if (s.d == 128 && s.Bk == 128) return launch_fa<128, 128>(s, q, k, v, idx, cnt, out, sched, st);
+  if (s.d == 128 && s.Bk == 64) return launch_fa<128, 64>(s, q, k, v, idx, cnt, out, sched, st);
+  if (s.d == 64 && s.Bk == 128) return launch_fa<64, 128>(s, q, k, v, idx, cnt, out, sched, st);
+  return launch_fa<64, 64>(s, q, k, v, idx, cnt, out, sched, st);
 }
 
 }  // namespace rra

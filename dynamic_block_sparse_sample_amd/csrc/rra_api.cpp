@@ -17,6 +17,16 @@ bool empty_problem(const rra_params_t* p) { return p->batch == 0 || p->seq_len =
 
 rra_status_t check(const rra_params_t* p) { return rra_validate(p); }
 
+// The optional schedule workspace of the attention calls: nullptr, or at
+// least kSchedBytes, 16-byte aligned.
+rra_status_t sched_of(void* workspace, size_t workspace_bytes, uint32_t** sched) {
+  *sched = nullptr;
+  if (workspace == nullptr) return RRA_OK;
+  if (!aligned16(workspace) || workspace_bytes < rra::kSchedBytes) return RRA_ERR_WORKSPACE;
+  *sched = static_cast<uint32_t*>(workspace);
+  return RRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,28 +119,35 @@ rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k,
 }
 
 rra_status_t rra_sparse_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
-                             const int32_t* idx, const int32_t* cnt, void* out, void* stream) {
+                             const int32_t* idx, const int32_t* cnt, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   rra_status_t st = check(p);
   if (st != RRA_OK) return st;
   if (empty_problem(p)) return RRA_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(idx) || !ok_ptr(cnt) || !ok_ptr(out))
     return RRA_ERR_INVALID_ARG;
+  uint32_t* sched = nullptr;
+  st = sched_of(workspace, workspace_bytes, &sched);
+  if (st != RRA_OK) return st;
   const rra::Shape s = rra::shape_of(*p);
   return hip_status(rra::launch_flash_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                            static_cast<const uint16_t*>(v), idx, cnt,
-                                           static_cast<uint16_t*>(out), stream));
+                                           static_cast<uint16_t*>(out), sched, stream));
 }
 
 rra_status_t rra_dense_attn(const rra_params_t* p, const void* q, const void* k, const void* v, void* out,
-                            void* stream) {
+                            void* workspace, size_t workspace_bytes, void* stream) {
   rra_status_t st = check(p);
   if (st != RRA_OK) return st;
   if (empty_problem(p)) return RRA_OK;
   if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(out)) return RRA_ERR_INVALID_ARG;
+  uint32_t* sched = nullptr;
+  st = sched_of(workspace, workspace_bytes, &sched);
+  if (st != RRA_OK) return st;
   const rra::Shape s = rra::shape_of(*p);
   return hip_status(rra::launch_flash_attn(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                            static_cast<const uint16_t*>(v), nullptr, nullptr,
-                                           static_cast<uint16_t*>(out), stream));
+                                           static_cast<uint16_t*>(out), sched, stream));
 }
 
 }  // extern "C"

@@ -12,6 +12,12 @@ namespace rra {
 // Largest number of blocks per row (the selection kernel holds a row in registers).
 constexpr int kMaxBlocks = 4096;
 
+// Dynamic schedule of the attention kernel: one work counter per XCD, each on
+// its own 128-byte line.
+constexpr int kSchedQueues = 8;
+constexpr int kSchedStride = 32;  // uint32 words between counters
+constexpr size_t kSchedBytes = sizeof(uint32_t) * kSchedQueues * kSchedStride;
+
 struct Shape {
   int Bz, H, Hkv, L, d, S, Bk;
   int G;   // H / Hkv
@@ -40,8 +46,10 @@ int launch_top_tau(const Shape& s, float tau, int protect_last, const float* sco
                    int32_t* idx, int32_t* cnt, void* stream);
 int launch_xattn_scores(const Shape& s, const uint16_t* q, const uint16_t* k, float* score, void* stream);
 int launch_block_mass(const Shape& s, const uint16_t* q, const uint16_t* k, float* mass, void* stream);
+// sched: kSchedBytes of device memory for the dynamic schedule, or nullptr
+// for one workgroup per (b, h, I) row.
 int launch_flash_attn(const Shape& s, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const int32_t* idx, const int32_t* cnt, uint16_t* out, void* stream);
+                      const int32_t* idx, const int32_t* cnt, uint16_t* out, uint32_t* sched, void* stream);
 
 }  // namespace rra
 

@@ -99,4 +99,12 @@ rra_status_t rra_estimate_workspace_size(const rra_params_t* p, size_t* bytes) {
   return RRA_OK;
 }
 
+rra_status_t rra_attn_workspace_size(const rra_params_t* p, size_t* bytes) {
+  if (bytes == nullptr) return RRA_ERR_INVALID_ARG;
+  rra_status_t st = rra_validate(p);
+  if (st != RRA_OK) return st;
+  *bytes = rra::kSchedBytes;
+  return RRA_OK;
+}
+
 }  // extern "C"

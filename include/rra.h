@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define RRA_ABI_VERSION 2
+#define RRA_ABI_VERSION 3
 
 typedef enum rra_status {
   RRA_OK = 0,
@@ -104,6 +104,10 @@ rra_status_t rra_validate(const rra_params_t* p);
 
 /* Bytes of device workspace rra_estimate needs (*bytes is written). */
 rra_status_t rra_estimate_workspace_size(const rra_params_t* p, size_t* bytes);
+
+/* Bytes of the optional device workspace of rra_sparse_attn and
+ * rra_dense_attn (*bytes is written; the same for every valid problem). */
+rra_status_t rra_attn_workspace_size(const rra_params_t* p, size_t* bytes);
 
 /* Round n float32 values to bfloat16, round to nearest even (used when
  * inputs arrive in float32; the method itself runs on bf16). */
@@ -182,15 +186,26 @@ rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k,
  * key-block indices in [0, I] ([0, Nb) when causal = 0) with
  * 1 <= cnt <= I + 1 (Nb) (rra_top_tau's output satisfies this; other lists
  * are the caller's responsibility).  bf16 MFMA, float32 accumulation and
- * online softmax; out is rounded to bf16. */
+ * online softmax; out is rounded to bf16.
+ *
+ * workspace (optional, rra_attn_workspace_size() bytes, 16-byte aligned)
+ * holds the counters of a dynamic schedule: a fixed set of resident
+ * workgroups takes the (b, h, I) rows from one queue per XCD and, once its
+ * own queue is empty, from the others, so XCDs that run slower (their clocks
+ * differ under the power limit) are not left to finish the launch alone.
+ * Its contents on entry do not matter and are unspecified on return; calls
+ * that may run at the same time need distinct workspaces.  workspace = NULL
+ * launches one workgroup per row instead.  The output is bitwise the same
+ * either way.  A workspace smaller than required returns RRA_ERR_WORKSPACE. */
 rra_status_t rra_sparse_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
-                             const int32_t* idx, const int32_t* cnt, void* out, void* stream);
+                             const int32_t* idx, const int32_t* cnt, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* Dense flash attention: rra_sparse_attn with every causal key block (every
  * key block when causal = 0) selected (the FlashAttention baseline of
- * §4.1), same kernel. */
+ * §4.1), same kernel and the same optional workspace. */
 rra_status_t rra_dense_attn(const rra_params_t* p, const void* q, const void* k, const void* v,
-                            void* out, void* stream);
+                            void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = rra.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -58,7 +58,7 @@ def test_params_struct_matches_header():
 
 
 def test_abi_version_and_status_strings():
-    assert rra.lib().rra_abi_version() == 2
+    assert rra.lib().rra_abi_version() == 3
     for code in range(5):
         assert rra.status_str(code).startswith("RRA_")
     assert rra.status_str(99) == "RRA_ERR_UNKNOWN"
@@ -143,8 +143,8 @@ def test_entry_points_reject_null_and_misaligned_pointers_without_launching():
     assert lib.rra_stride_aggregate(by(p), odd, fake, s) == 1
     assert lib.rra_block_scores(by(p), fake, null, fake, s) == 1
     assert lib.rra_top_tau(by(p), fake, fake, null, fake, s) == 1
-    assert lib.rra_sparse_attn(by(p), fake, fake, fake, fake, null, fake, s) == 1
-    assert lib.rra_dense_attn(by(p), fake, fake, fake, odd, s) == 1
+    assert lib.rra_sparse_attn(by(p), fake, fake, fake, fake, null, fake, null, 0, s) == 1
+    assert lib.rra_dense_attn(by(p), fake, fake, fake, odd, null, 0, s) == 1
     assert lib.rra_block_mass(by(p), fake, null, fake, s) == 1
     assert lib.rra_block_mass(by(p), fake, fake, odd, s) == 1
     assert lib.rra_block_mass(by(P(head_dim=96)), fake, fake, fake, s) == 2
@@ -162,7 +162,22 @@ def test_entry_points_reject_null_and_misaligned_pointers_without_launching():
     # invalid parameters win over everything else
     bad = P(head_dim=96)
     assert lib.rra_estimate(by(bad), fake, fake, fake, 1 << 40, fake, fake, fake, null, s) == 2
-    assert lib.rra_dense_attn(None, fake, fake, fake, fake, s) == 1
+    assert lib.rra_dense_attn(None, fake, fake, fake, fake, null, 0, s) == 1
+    # the attention calls' optional schedule workspace: too small or misaligned
+    wneed = rra.attn_workspace_size(p)
+    assert lib.rra_sparse_attn(by(p), fake, fake, fake, fake, fake, fake, fake, wneed - 1, s) == 3
+    assert lib.rra_sparse_attn(by(p), fake, fake, fake, fake, fake, fake, odd, wneed, s) == 3
+    assert lib.rra_dense_attn(by(p), fake, fake, fake, fake, fake, 0, s) == 3
+    assert lib.rra_dense_attn(by(bad), fake, fake, fake, fake, fake, 0, s) == 2
+
+
+def test_attn_workspace_size():
+    """The attention schedule needs one 128-byte counter line per XCD (8), for any valid problem."""
+    assert rra.attn_workspace_size(P()) == 1024
+    assert rra.attn_workspace_size(P(seq_len=8001, causal=False)) == 1024
+    assert rra.attn_workspace_size(P(batch=0)) == 1024
+    with pytest.raises(rra.RRAError):
+        rra.attn_workspace_size(P(head_dim=96))
 
 
 def test_empty_problem_is_a_no_op_even_with_null_pointers():
@@ -170,8 +185,8 @@ def test_empty_problem_is_a_no_op_even_with_null_pointers():
     p = P(batch=0)
     by = ctypes.byref
     assert lib.rra_estimate(by(p), None, None, None, 0, None, None, None, None, None) == 0
-    assert lib.rra_sparse_attn(by(p), None, None, None, None, None, None, None) == 0
-    assert lib.rra_dense_attn(by(p), None, None, None, None, None) == 0
+    assert lib.rra_sparse_attn(by(p), None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.rra_dense_attn(by(p), None, None, None, None, None, 0, None) == 0
     assert lib.rra_stride_aggregate(by(p), None, None, None) == 0
     assert lib.rra_block_scores(by(p), None, None, None, None) == 0
     assert lib.rra_top_tau(by(p), None, None, None, None, None) == 0

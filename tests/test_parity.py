@@ -248,7 +248,7 @@ def test_protect_last_flag_and_empty_problem():
     assert torch.equal(sel.cnt[..., :-1], sel0.cnt[..., :-1])
     # empty problem: nothing to do, nothing written
     pe = rra.make_params(0, 4, 2, 2048, 128, 16, 128, 0.5)
-    assert rra.lib().rra_dense_attn(ctypes.byref(pe), None, None, None, None, None) == 0
+    assert rra.lib().rra_dense_attn(ctypes.byref(pe), None, None, None, None, None, 0, None) == 0
     e = torch.empty(0, 4, 2048, 128, dtype=torch.bfloat16, device="cuda")
     ek = torch.empty(0, 2, 2048, 128, dtype=torch.bfloat16, device="cuda")
     assert rra.dense_attn(pe, e, ek, ek).shape == e.shape
