@@ -247,7 +247,7 @@ def main(argv=None) -> int:
     sum_cnt = int(cnt.sum())
     causal_blocks = p.batch * p.num_heads * nb * (nb + 1) // 2
     density = sum_cnt / causal_blocks
-    # per head (SURVEY-style report: min / median / max), and without the protected last row
+    # per head (min / median / max), and without the protected last row
     per_head = (cnt.double().sum(-1) / (nb * (nb + 1) / 2)).flatten().sort().values
     dens_no_last = (sum_cnt - int(cnt[..., -1].sum())) / (p.batch * p.num_heads * nb * (nb - 1) / 2) if nb > 1 else 1.0
     # exact unmasked work: a selected diagonal block has Bk (Bk + 1) / 2 causal (t, u) pairs, not Bk^2
