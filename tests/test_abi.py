@@ -192,3 +192,23 @@ def test_empty_problem_is_a_no_op_even_with_null_pointers():
     assert lib.rra_top_tau(by(p), None, None, None, None, None) == 0
     assert lib.rra_block_mass(by(p), None, None, None, None) == 0
     assert lib.rra_xattn_block_scores(by(p), None, None, None, None) == 0
+
+
+def test_header_compiles_as_c_and_host_calls_work(tmp_path):
+    """include/rra.h compiles as strict C11 and a C program linked against
+    librra.so gets the documented results from the host-only entry points."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    src = os.path.join(ROOT, "tests", "c_abi", "host_calls.c")
+    exe = str(tmp_path / "host_calls")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.join(ROOT, 'include')}",
+           src, "-o", exe, f"-L{libdir}", "-lrra", f"-Wl,-rpath,{libdir}"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    assert run.stdout.strip() == "ok"
