@@ -121,16 +121,6 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t* gbase, int voff, ui
       : "memory", "scc");
 }
 
-// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N-1>), unrolled.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }

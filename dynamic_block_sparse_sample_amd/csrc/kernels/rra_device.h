@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 namespace rra {
 
@@ -88,6 +89,18 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 2) v += dpp<kDppXor1>(v);
   if constexpr (N >= 4) v += dpp<kDppXor2>(v);
   return v;
+}
+
+// f(std::integral_constant<int, 0>) ... f(std::integral_constant<int, N-1>),
+// unrolled at compile time (indices stay constants, so per-index register
+// arrays and immediates stay in registers and instructions).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace rra

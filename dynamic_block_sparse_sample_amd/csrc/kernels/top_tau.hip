@@ -20,7 +20,6 @@
 // Ranks among equal scores and the ascending compaction of the selected J
 // come from per-slot ballots (a popcount of the lanes below).
 #include <cmath>
-#include <utility>
 
 #include "../rra_internal.h"
 #include "rra_device.h"
@@ -59,17 +58,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
          __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi32[1]) << 32) | lo32[1]));
 }
 
-// f(integral_constant<k>) for k = 0 .. N-1, unrolled at compile time (the
-// per-slot arrays must stay in registers).
-template <typename F, int... K>
-__device__ __forceinline__ void for_slots_impl(F&& f, std::integer_sequence<int, K...>) {
-  (f(std::integral_constant<int, K>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void for_slots(F&& f) {
-  for_slots_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Lanes below this one among the set bits of a ballot.
 __device__ __forceinline__ int lanes_below(uint64_t ballot) {
   return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(ballot >> 32),
@@ -91,7 +79,7 @@ __device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint
     else return static_cast<double>(__uint_as_float(bits[k]));
   };
   double total = 0.0;
-  for_slots<NS>([&](auto kc) {
+  static_for<NS>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     const int J = k * 64 + lane;
     const float v = J < n ? srow[J] : 0.0f;
@@ -116,7 +104,7 @@ __device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint
   for (int bit = 30; bit >= 0; --bit) {
     const uint32_t cand = x | (1u << bit);
     double s = 0.0;
-    for_slots<NS>([&](auto kc) {
+    static_for<NS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       s += bits[k] >= cand ? value(kc) : 0.0;
     });
@@ -127,7 +115,7 @@ __device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint
   // Blocks above t, and the number of blocks equal to t.
   double above = 0.0;
   int n_eq = 0;
-  for_slots<NS>([&](auto kc) {
+  static_for<NS>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     above += bits[k] > x ? value(kc) : 0.0;
     n_eq += __popcll(__ballot(bits[k] == x));
@@ -146,7 +134,7 @@ __device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint
 
   // Mask row, and the selected J compacted in ascending order.
   int eq_before = 0, sel_before = 0;
-  for_slots<NS>([&](auto kc) {
+  static_for<NS>([&](auto kc) {
     constexpr int k = decltype(kc)::value;
     const int J = k * 64 + lane;
     const bool eq = bits[k] == x;
