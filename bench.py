@@ -257,12 +257,6 @@ def main(argv=None) -> int:
     f_sel = 4.0 * d * Bk * Bk * sum_cnt
     achieved = f_sel / (t_sp * 1e-3) / 1e12
     value = f_dense / (ms_step * 1e-3) / 1e12
-    # algorithmic bytes of the estimator and of the aggregation kernel
-    ns = p.num_strides
-    k_bytes = w.batch * w.num_kv_heads * L * d * 2
-    kagg_b = w.batch * w.num_kv_heads * ns * d * 2
-    est_bytes = (k_bytes + w.batch * w.num_heads * ns * d * 2 + w.batch * w.num_heads * nb * nb
-                 + 4 * sum_cnt + 4 * w.batch * w.num_heads * nb)
     traffic = None
     if os.path.exists(args.traffic_json):
         try:
@@ -301,15 +295,7 @@ def main(argv=None) -> int:
         "sparse_attn_unmasked_tflops": round(
             (f_sel - 4.0 * d * diag_sel * (Bk * Bk - Bk * (Bk + 1) / 2)) / (t_sp * 1e-3) / 1e12, 2),
         "estimator_kernels_ms": {kk: round(vv, 4) for kk, vv in brk.items()},
-        "estimator_hbm_frac": round(est_bytes / (t_est * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        # max(bytes / BW, executed flops / P_bf16) / t: the two-pass scores execute
-        # 2 * 2d * Bz * H * Ns (Ns + 1) / 2 flops (the exps bind less on this part)
-        "estimator_binding_roofline_frac": round(
-            max(est_bytes / (PEAK_HBM_GBS * 1e9),
-                2 * 2.0 * d * w.batch * w.num_heads * ns * (ns + 1) / 2 / (PEAK_BF16_TFLOPS * 1e12))
-            / (t_est * 1e-3), 4),
-        "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (brk["stride_aggregate"] * 1e-3) / 1e9
-                                           / PEAK_HBM_GBS, 4),
+        **estimator_fracs(p, sum_cnt, t_est, brk["stride_aggregate"]),
         "dense_attn_tflops": round(f_dense / (t_dense * 1e-3) / 1e12, 2),
         "roofline": {"kernel": "flash_attn_kernel<128,128> (rra_sparse_attn)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -372,49 +358,99 @@ SELECTION_POINTS = {
 }
 
 
+def estimator_fracs(p, sum_cnt: int, t_est_ms: float, t_agg_ms: float) -> dict:
+    """Roofline fractions of the estimator and of its aggregation kernel.
+
+    Algorithmic bytes of the estimator: K read once, the sampled queries, the
+    mask, index lists and counts written (Kagg and block-score round trips are
+    intermediates).  Binding roofline: max(bytes / BW, executed flops / P_bf16)
+    / t, the two-pass scores executing 2 * 2d * Bz * H * Ns (Ns + 1) / 2 flops.
+    Aggregation: K read + Kagg written over its own time."""
+    L, d, nb, ns = p.seq_len, p.head_dim, p.num_blocks, p.num_strides
+    k_bytes = p.batch * p.num_kv_heads * L * d * 2
+    kagg_b = p.batch * p.num_kv_heads * ns * d * 2
+    est_bytes = (k_bytes + p.batch * p.num_heads * ns * d * 2 + p.batch * p.num_heads * nb * nb
+                 + 4 * sum_cnt + 4 * p.batch * p.num_heads * nb)
+    flops2 = 2 * 2.0 * d * p.batch * p.num_heads * ns * (ns + 1) / 2
+    return {
+        "estimator_hbm_frac": round(est_bytes / (t_est_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "estimator_binding_roofline_frac": round(
+            max(est_bytes / (PEAK_HBM_GBS * 1e9), flops2 / (PEAK_BF16_TFLOPS * 1e12)) / (t_est_ms * 1e-3), 4),
+        "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (t_agg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
 def workloads_report(reps=5):
-    """Estimator, sparse and dense attention times of every bf16 workload."""
+    """Every configuration point at its own settings: the five workloads, and
+    the 32K one swept over S in {8, 16, 32} x tau in {0.8, 0.9, 0.95}.  Per
+    point: the estimator and its aggregation kernel, sparse and dense attention
+    (event-timed averages of `reps` launches), density, TFLOP/s and roofline
+    fractions.  fp32 workloads are cast to bf16 on the GPU first (timed apart)."""
     import torch
 
     import dynamic_block_sparse_sample_amd as rra
     from dynamic_block_sparse_sample_amd import workloads as wl
 
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
     for name, w in wl.WORKLOADS.items():
-        if w.fp32_inputs:
-            continue
         log(f"[workloads] {name}")
         q, k, v = wl.make_inputs(w)
-        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        t_cast = None
+        if w.fp32_inputs:
+            q32, k32, v32 = q.cuda(), k.cuda(), v.cuda()
+            qd, kd, vd = (torch.empty(t.shape, dtype=torch.bfloat16, device="cuda") for t in (q32, k32, v32))
+            t_cast = timed(lambda: [rra.cast_f32_to_bf16(s_, d_) for s_, d_ in ((q32, qd), (k32, kd), (v32, vd))])
+            del q32, k32, v32
+        else:
+            qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
         del q, k, v
-        p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block, w.tau)
-        ws = rra.alloc_workspace(p, qd.device)
-        sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
+        sweep = [(S, tau) for S in (8, 16, 32) for tau in (0.8, 0.9, 0.95)] if name == "llama_32k" else [
+            (w.stride, w.tau)]
         out = torch.empty_like(qd)
-        times = {}
-        for tag, fn in (("estimate", lambda: rra.estimate(p, qd, kd, workspace=ws, out=sel)),
-                        ("sparse_attn", lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)),
-                        ("dense_attn", lambda: rra.dense_attn(p, qd, kd, vd, out=out))):
-            fn()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(reps):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            times[tag] = a.elapsed_time(b) / reps
-        nb = p.num_blocks
-        sum_cnt = int(sel.cnt.sum())
-        f_sel = 4.0 * w.head_dim * w.block * w.block * sum_cnt
-        f_full = 4.0 * w.head_dim * w.block * w.block * w.batch * w.num_heads * nb * (nb + 1) / 2
-        yield {"mode": "workloads", "workload": name, "seq_len": w.seq_len, "heads": f"{w.num_heads}/{w.num_kv_heads}",
-               "stride": w.stride, "tau": w.tau, "density": round(sum_cnt / (w.batch * w.num_heads * nb * (nb + 1) / 2), 4),
-               "t_estimate_ms": round(times["estimate"], 4), "t_sparse_attn_ms": round(times["sparse_attn"], 4),
-               "t_dense_attn_ms": round(times["dense_attn"], 4),
-               "sparse_tflops": round(f_sel / (times["sparse_attn"] * 1e-3) / 1e12, 1),
-               "dense_tflops": round(f_full / (times["dense_attn"] * 1e-3) / 1e12, 1),
-               "speedup_vs_dense": round(times["dense_attn"] / (times["estimate"] + times["sparse_attn"]), 3)}
-        del qd, kd, vd, out, ws, sel
+        t_dense = None
+        for S, tau in sweep:
+            p = rra.make_params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, tau)
+            ws = rra.alloc_workspace(p, qd.device)
+            sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
+            kagg = torch.empty((p.batch, p.num_kv_heads, p.num_strides, p.head_dim), dtype=torch.bfloat16,
+                               device=qd.device)
+            t_est = timed(lambda: rra.estimate(p, qd, kd, workspace=ws, out=sel))
+            t_agg = timed(lambda: rra.stride_aggregate(p, kd, kagg))
+            t_sp = timed(lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out))
+            if t_dense is None:  # depends on the shape only
+                t_dense = timed(lambda: rra.dense_attn(p, qd, kd, vd, out=out))
+            nb = p.num_blocks
+            sum_cnt = int(sel.cnt.sum())
+            f_sel = 4.0 * w.head_dim * w.block * w.block * sum_cnt
+            f_full = 4.0 * w.head_dim * w.block * w.block * w.batch * w.num_heads * nb * (nb + 1) / 2
+            f_dense = 4.0 * w.head_dim * w.batch * w.num_heads * w.seq_len * (w.seq_len + 1) / 2
+            line = {"mode": "workloads", "workload": name, "seq_len": w.seq_len,
+                    "heads": f"{w.num_heads}/{w.num_kv_heads}", "head_dim": w.head_dim, "block": w.block,
+                    "stride": S, "tau": tau,
+                    "density": round(sum_cnt / (w.batch * w.num_heads * nb * (nb + 1) / 2), 4),
+                    "t_estimate_ms": round(t_est, 4), "t_stride_aggregate_ms": round(t_agg, 4),
+                    "t_sparse_attn_ms": round(t_sp, 4), "t_dense_attn_ms": round(t_dense, 4),
+                    "sparse_tflops": round(f_sel / (t_sp * 1e-3) / 1e12, 1),
+                    "sparse_mfma_frac": round(f_sel / (t_sp * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "dense_tflops": round(f_full / (t_dense * 1e-3) / 1e12, 1),
+                    "effective_tflops": round(f_dense / ((t_est + t_sp) * 1e-3) / 1e12, 1),
+                    "speedup_vs_dense": round(t_dense / (t_est + t_sp), 3),
+                    **estimator_fracs(p, sum_cnt, t_est, t_agg)}
+            if t_cast is not None:
+                line["t_cast_f32_to_bf16_ms"] = round(t_cast, 4)
+            yield line
+            del ws, sel, kagg
+        del qd, kd, vd, out
         torch.cuda.empty_cache()
 
 
