@@ -13,7 +13,8 @@
 // two, that hold its candidates).  Scores are non-negative, so their float bit
 // patterns order like the values; the threshold value t is found by a
 // bitwise search over those 31 bits: t = the largest x with
-// sum(scores >= x) >= tau * T (float64 sums, one wave reduction per bit).
+// sum(scores >= x) >= tau * T (float32 sums, one wave reduction per bit, the
+// answer then confirmed with two float64 sums, or searched again in float64).
 // Every block scoring above t is then selected (their sum is below tau * T),
 // and of the blocks equal to t the m lowest J, m the smallest count with
 // sum(above) + m * t >= tau * T: exactly the prefix of the sorted order.
@@ -98,18 +99,41 @@ __device__ __forceinline__ void top_tau_row(const float* __restrict__ srow, uint
   }
 
   // Threshold bits: the largest x with sum(bits >= x) >= tau * T (x >= 1,
-  // since the positive scores sum to T >= tau * T).
+  // since the positive scores sum to T >= tau * T).  The bitwise search runs
+  // on float32 sums (cheap); its answer is then checked exactly in float64:
+  // sum(>= x) >= tau * T > sum(> x) makes x the largest such value (the sum
+  // only falls as x grows).  A row where float32 rounding decided a step
+  // differently (a sum within ~1e-6 of tau * T) repeats the search in float64.
   const double thr = tau * total;
-  uint32_t x = 0;
-  for (int bit = 30; bit >= 0; --bit) {
-    const uint32_t cand = x | (1u << bit);
+  auto sum_ge = [&](uint32_t cand) {
     double s = 0.0;
     static_for<NS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       s += bits[k] >= cand ? value(kc) : 0.0;
     });
-    s = wave_sum_d(s);
-    if (__builtin_amdgcn_readfirstlane(s >= thr ? 1 : 0)) x = cand;
+    return wave_sum_d(s);
+  };
+  uint32_t x = 0;
+  {
+    const float thr32 = static_cast<float>(thr);
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = x | (1u << bit);
+      float s = 0.0f;
+      static_for<NS>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        s += bits[k] >= cand ? __uint_as_float(bits[k]) : 0.0f;
+      });
+      s = sum_halves(group_sum<32>(s));
+      if (__builtin_amdgcn_readfirstlane(s >= thr32 ? 1 : 0)) x = cand;
+    }
+  }
+  const bool exact = x >= 1 && sum_ge(x) >= thr && !(x < 0x7F800000u && sum_ge(x + 1) >= thr);
+  if (!__builtin_amdgcn_readfirstlane(exact ? 1 : 0)) {
+    x = 0;
+    for (int bit = 30; bit >= 0; --bit) {
+      const uint32_t cand = x | (1u << bit);
+      if (__builtin_amdgcn_readfirstlane(sum_ge(cand) >= thr ? 1 : 0)) x = cand;
+    }
   }
 
   // Blocks above t, and the number of blocks equal to t.
