@@ -44,11 +44,11 @@
 // Without causality every key block is a candidate and only keys beyond the
 // sequence are masked.
 //
-// Work order: KV groups in phases small enough for the memory-side cache;
-// inside a phase longest rows (largest I) first (item w goes to XCD w mod 8),
-// the heads of a group adjacent so that they stream the same K/V through one
-// L2, the group served by an XCD rotating every 16 slots so that denser
-// groups do not leave other XCDs idle.
+// Work order (fa_order.h): KV groups in phases small enough for the
+// memory-side cache; inside a phase longest rows (largest I) first (item w
+// goes to XCD w mod 8), the heads of a group adjacent so that they stream the
+// same K/V through one L2, the group served by an XCD rotating every 16 slots
+// so that denser groups do not leave other XCDs idle.
 //
 // Schedule: with a counter workspace the grid is the resident workgroups
 // (occupancy x CUs, workgroup w on XCD w mod 8); each takes items w = 8k + x
@@ -64,6 +64,7 @@
 #include <utility>
 
 #include "../rra_internal.h"
+#include "fa_order.h"
 #include "rra_device.h"
 
 namespace rra {
@@ -166,35 +167,8 @@ __global__ __launch_bounds__((BLK / 32) * 64, BLK == 128 ? 2 : 1) void flash_att
 
   // ---- one work item: (b, h, I) from the item index w ----
   auto run_item = [&](const int w) {
-    // Item w runs on XCD w mod 8.  The KV groups are processed in phases of
-    // `gp` groups (their K and V fit the memory-side cache together); inside a
-    // phase XCD x takes every (8/gp)-th query block, longest rows first, the
-    // heads of a group next to each other (they stream the same K/V through the
-    // XCD's L2).  The group an XCD serves rotates every 16 slots (about the
-    // workgroups an XCD holds at once, so neighbouring query blocks of a group,
-    // whose lists overlap, still share the L2): groups differ in density, and a
-    // fixed assignment would leave the XCDs of the sparser groups idle at the end.
-    int bg, hh, I;
-    {
-      if (gp > 0) {
-        const int phase_items = gp * G * Nb;
-        const int ph = w / phase_items;
-        const int r = w % phase_items;
-        const int xcd = r & 7;
-        int slot = r >> 3;
-        const int split = 8 / gp;
-        hh = slot % G;
-        slot /= G;
-        I = Nb - 1 - (slot * split + xcd / gp);
-        bg = ph * gp + (xcd + (slot >> 4)) % gp;
-      } else {
-        int t = w;
-        hh = t % G;
-        t /= G;
-        bg = t % nbg;
-        I = Nb - 1 - t / nbg;
-      }
-    }
+    const FaItem it = fa_item(w, gp, G, Nb, nbg);
+    const int bg = it.bg, hh = it.hh, I = it.I;
     const int b = bg / Hkv;
     const int g = bg % Hkv;
     const int h = g * G + hh;
@@ -534,24 +508,8 @@ __global__ void sched_clear_kernel(uint32_t* __restrict__ sched) {
   for (int i = threadIdx.x; i < kSchedQueues * kSchedStride; i += blockDim.x) sched[i] = 0u;
 }
 
-// Groups per phase of the work order: the largest gp in {8, 4, 2, 1} that
-// divides the group count, splits the query blocks evenly over 8/gp XCDs, and
-// keeps gp groups' K and V within the budget.  0 = plain order.  Budgets
-// (measured on the 32K / 64K / 128K workloads): dense launches read each
-// group's K and V in step across its rows and do best with phases of up to
-// half the 256 MB memory-side cache; sparse launches re-read K/V blocks
-// scattered by their lists and do best with a quarter (at 128K one group per
-// phase: sparse 1.2 % faster, dense 0.8 % slower than with two).
-constexpr int64_t kDensePhaseBytes = int64_t(128) << 20;
-constexpr int64_t kSparsePhaseBytes = int64_t(64) << 20;
-
 static int phase_groups(const Shape& s, int64_t budget) {
-  const int nbg = s.Bz * s.Hkv;
-  const int64_t kv_bytes = int64_t(2) * s.L * s.d * 2;
-  for (int gp = 8; gp >= 1; gp >>= 1) {
-    if (nbg % gp == 0 && s.Nb % (8 / gp) == 0 && gp * kv_bytes <= budget) return gp;
-  }
-  return s.Nb % 8 == 0 ? 1 : 0;  // one group per phase even above the budget
+  return fa_phase_groups(s.Bz * s.Hkv, s.Nb, int64_t(2) * s.L * s.d * 2, budget);
 }
 
 // Workgroups of flash_attn_kernel<D, BLK> resident at once on the current
