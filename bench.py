@@ -656,11 +656,16 @@ def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
 
 
 def _kernel_hash() -> str:
-    """Hash of the attention kernel source; traffic counters are only valid for it."""
+    """Hash of the attention kernel source (flash_attn.hip and its work-order
+    header fa_order.h); traffic counters are only valid for it."""
     import hashlib
-    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd", "csrc",
-                       "kernels", "flash_attn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    kdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd", "csrc",
+                        "kernels")
+    h = hashlib.sha256()
+    for name in ("flash_attn.hip", "fa_order.h"):
+        with open(os.path.join(kdir, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":
