@@ -184,9 +184,12 @@ rra_status_t rra_block_mass(const rra_params_t* p, const void* q, const void* k,
  *   A(t) = { u <= t, u < L : block(u) in idx[b,h,I,0:cnt[b,h,I]] }
  * (without u <= t when causal = 0).  idx rows must be strictly ascending
  * key-block indices in [0, I] ([0, Nb) when causal = 0) with
- * 1 <= cnt <= I + 1 (Nb) (rra_top_tau's output satisfies this; other lists
- * are the caller's responsibility).  bf16 MFMA, float32 accumulation and
- * online softmax; out is rounded to bf16.
+ * 1 <= cnt <= I + 1 (Nb) (rra_top_tau's output satisfies this).  The lists
+ * are device data and are not checked: the kernel reads the K / V rows of
+ * whatever blocks they name, so an index outside the range reads outside K
+ * and V, and a repeated one counts its block twice; cnt = 0 gives a zero
+ * output row.  bf16 MFMA, float32 accumulation and online softmax; out is
+ * rounded to bf16.
  *
  * workspace (optional, rra_attn_workspace_size() bytes, 16-byte aligned)
  * holds the counters of a dynamic schedule: a fixed set of resident
