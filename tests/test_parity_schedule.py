@@ -8,8 +8,9 @@ bit for bit: on every kernel template (d 64/128, Bk 64/128), ragged and
 non-causal shapes, sparse and dense, with rows enough to exceed the resident
 workgroups (so the queues and the stealing run).  The workspace's contents on
 entry must not matter, one workspace serves consecutive calls, and a short
-one is refused before anything is launched.  (Agreement of these outputs
-with the oracle is the business of the other parity tests.)
+one is refused before anything is launched.  Rows whose list is empty
+(cnt = 0) come out as zeros without disturbing the others.  (Agreement of
+these outputs with the oracle is the business of the other parity tests.)
 """
 import ctypes
 
@@ -89,3 +90,27 @@ def test_short_workspace_is_refused():
     assert ei.value.code == 3
     n = ctypes.c_size_t(0)
     assert rra.lib().rra_attn_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0 and n.value == 1024
+
+
+@pytest.mark.parametrize("schedule", ["dynamic", "static"])
+def test_empty_lists_give_zero_rows(schedule):
+    """cnt = 0 rows (no block selected) come out as zeros; every other row is
+    bitwise what it is with the lists untouched."""
+    B, H, Hkv, L, d, S, Bk = 1, 8, 2, 4096 + 40, 128, 16, 128
+    q, k, v = wl.make_random(B, H, Hkv, L, d, seed=5, scale=1.5, diag=1.0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    p = rra.make_params(B, H, Hkv, L, d, S, Bk, 0.9)
+    sel = rra.estimate(p, qd, kd)
+    ref = rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, schedule=schedule)
+    cnt = sel.cnt.clone()
+    zero_rows = [(0, 0, 0), (0, 3, 7), (0, 5, p.num_blocks - 1), (0, 7, 20)]
+    for b, h, i in zero_rows:
+        cnt[b, h, i] = 0
+    out = rra.sparse_attn(p, qd, kd, vd, sel.idx, cnt, schedule=schedule)
+    torch.cuda.synchronize()
+    keep = torch.ones((B, H, L), dtype=torch.bool, device="cuda")
+    for b, h, i in zero_rows:
+        rows = slice(i * Bk, min((i + 1) * Bk, L))
+        assert torch.count_nonzero(out[b, h, rows]).item() == 0
+        keep[b, h, rows] = False
+    assert torch.equal(out[keep], ref[keep])
