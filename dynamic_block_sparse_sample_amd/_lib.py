@@ -154,6 +154,17 @@ def _need(t: torch.Tensor, name: str, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _workspace_bytes(t: torch.Tensor, name: str) -> int:
+    """Size in bytes of a caller-supplied workspace (any dtype): a contiguous device tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.numel() * t.element_size()
+
+
 def _shapes(p: Params):
     q = (p.batch, p.num_heads, p.seq_len, p.head_dim)
     kv = (p.batch, p.num_kv_heads, p.seq_len, p.head_dim)
@@ -269,8 +280,9 @@ def estimate(p: Params, q: torch.Tensor, k: torch.Tensor, workspace: torch.Tenso
     _selection_buffers(p, q.device, out.mask, out.idx, out.cnt)
     if out.score is not None:
         _need(out.score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
+    ws_bytes = _workspace_bytes(workspace, "workspace")
     _check("rra_estimate",
-           lib().rra_estimate(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(workspace), workspace.numel(),
+           lib().rra_estimate(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(workspace), ws_bytes,
                               _ptr(out.mask), _ptr(out.idx), _ptr(out.cnt), _ptr(out.score), _stream(stream)))
     return out
 
@@ -290,7 +302,7 @@ def _attn_workspace(p: Params, device, workspace, schedule: str):
         raise ValueError(f"schedule must be 'dynamic' or 'static', not {schedule!r}")
     if workspace is None:
         workspace = torch.empty(attn_workspace_size(p), dtype=torch.uint8, device=device)
-    return _ptr(workspace), workspace.numel() * workspace.element_size()
+    return _ptr(workspace), _workspace_bytes(workspace, "workspace")
 
 
 def sparse_attn(p: Params, q, k, v, idx, cnt, out=None, workspace=None, schedule="dynamic",

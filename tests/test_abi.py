@@ -212,3 +212,13 @@ def test_header_compiles_as_c_and_host_calls_work(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stderr
     assert run.stdout.strip() == "ok"
+
+
+def test_binding_workspace_checks_on_host():
+    """Workspaces handed to the binding are sized in bytes whatever their dtype,
+    and a host tensor is refused before any pointer reaches the library."""
+    import torch
+    with pytest.raises(ValueError, match="device tensor"):
+        _lib._workspace_bytes(torch.empty(1024, dtype=torch.uint8), "workspace")
+    with pytest.raises(TypeError):
+        _lib._workspace_bytes(bytearray(16), "workspace")

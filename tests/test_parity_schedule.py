@@ -114,3 +114,25 @@ def test_empty_lists_give_zero_rows(schedule):
         assert torch.count_nonzero(out[b, h, rows]).item() == 0
         keep[b, h, rows] = False
     assert torch.equal(out[keep], ref[keep])
+
+
+def test_workspaces_of_any_dtype_are_sized_in_bytes():
+    """A float32 workspace of the required bytes serves estimate and sparse
+    attention exactly like a uint8 one; host-memory workspaces are refused."""
+    B, H, Hkv, L, d, S, Bk = 1, 8, 2, 2048, 128, 16, 128
+    q, k, v = wl.make_random(B, H, Hkv, L, d, seed=9, scale=1.5, diag=1.0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    p = rra.make_params(B, H, Hkv, L, d, S, Bk, 0.9)
+    ref = rra.estimate(p, qd, kd)
+    ws32 = torch.empty((rra.workspace_size(p) + 3) // 4, dtype=torch.float32, device="cuda")
+    sel = rra.estimate(p, qd, kd, workspace=ws32)
+    a32 = torch.empty((rra.attn_workspace_size(p) + 3) // 4, dtype=torch.float32, device="cuda")
+    out = rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, workspace=a32)
+    want = rra.sparse_attn(p, qd, kd, vd, ref.idx, ref.cnt)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.mask, ref.mask) and torch.equal(sel.cnt, ref.cnt)
+    assert torch.equal(out, want)
+    with pytest.raises(ValueError):
+        rra.estimate(p, qd, kd, workspace=torch.empty(rra.workspace_size(p), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, workspace=torch.empty(1024, dtype=torch.uint8))
