@@ -55,7 +55,7 @@ const char* rra_status_str(rra_status_t status) {
   switch (status) {
     case RRA_OK: return "RRA_OK";
     case RRA_ERR_INVALID_ARG: return "RRA_ERR_INVALID_ARG: invalid parameter or pointer";
-    case RRA_ERR_UNSUPPORTED: return "RRA_ERR_UNSUPPORTED: shape or option not supported by this build";
+    case RRA_ERR_UNSUPPORTED: return "RRA_ERR_UNSUPPORTED: shape or option not supported by this library";
     case RRA_ERR_WORKSPACE: return "RRA_ERR_WORKSPACE: workspace missing or too small";
     case RRA_ERR_HIP: return "RRA_ERR_HIP: HIP runtime error";
   }
