@@ -96,7 +96,7 @@ def test_rr_positions_hand_worked_table():
 # ---------------------------------------------------------------------------
 def test_rr_variant_offsets_hand_worked_table():
     rows = [ln for ln in open(os.path.join(GOLDEN, "rr_variants.txt")) if ln.strip() and not ln.startswith("#")]
-    assert len(rows) == 13
+    assert len(rows) == 21
     for ln in rows:
         head, offs = ln.split("|")
         mode, H, S, layer, fixed = head.split()
@@ -151,6 +151,110 @@ def test_rr_variants_reach_the_block_scores():
     q_same = np.repeat(q[:, :1], H, axis=1)
     m_same = orc.block_scores(q_same, k, lay)
     assert all(np.array_equal(m_same[0, 0], m_same[0, h]) for h in range(H))
+
+
+def _golden_variant_rows():
+    rows = [ln for ln in open(os.path.join(GOLDEN, "rr_variants.txt")) if ln.strip() and not ln.startswith("#")]
+    out = []
+    for ln in rows:
+        head, offs = ln.split("|")
+        mode, H, S, layer, fixed = head.split()
+        out.append((mode, int(H), int(S), int(layer), int(fixed), [int(x) for x in offs.split()]))
+    return out
+
+
+def _scores_from_token_matrix(q_head, k_head, S, offsets_h, scale):
+    """Stride scores built from the full token score matrix by loops, RR §3.2:
+    the sampled query of stride i is the token at offset o inside that stride
+    (o from the hand-worked table), and its score against key stride j is the
+    mean over the stride's keys of the token scores, i.e.
+    (1/S) * sum_{t in stride j} scale * q[iS + o] . k[t], with j <= i visible."""
+    L = q_head.shape[0]
+    tok = scale * (torch.from_numpy(q_head) @ torch.from_numpy(k_head).T).numpy()  # [L, L]
+    ns = -(-L // S)
+    s = np.full((ns, ns), np.nan)
+    for i in range(ns):
+        pos = i * S + offsets_h
+        if pos >= L:
+            continue  # a partial last stride may not hold the sampled offset
+        for j in range(ns):
+            if j > i:
+                s[i, j] = -np.inf
+                continue
+            acc = 0.0
+            for t in range(j * S, min(j * S + S, L)):
+                acc += tok[pos, t]
+            s[i, j] = acc / S
+    return s
+
+
+def _mutant_stride_scores_without_offset(q_head, kagg, S, scale):
+    """A planted mistake: the first token of every stride sampled for every head."""
+    ns = kagg.shape[0]
+    s = scale * (q_head[np.arange(ns) * S] @ kagg.T)
+    s[np.triu_indices(ns, k=1)] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("S", [4, 8])
+def test_round_robin_gather_against_token_score_matrix(S):
+    """Pin of the sampled-query gather Q_P(i,h) (RR §3.1, §3.2; the abstract:
+    positions rotate across heads inside each stride): for every round-robin
+    strategy of the hand-worked table with H >= S, the oracle's stride scores
+    (exact key mean) equal the loop-built scores of the query at the table's
+    offset, on GQA shapes with a partial last stride.  The offset-dropping
+    mutant fails the same check."""
+    cases = [c for c in _golden_variant_rows() if c[2] == S and c[1] >= S]
+    assert {c[0] for c in cases} == {"head", "layer", "hybrid", "none"}
+    rng = np.random.default_rng(40 + S)
+    d = 8
+    for L in (8 * S, 8 * S + S // 2 + 1):
+        for mode, H, _, layer, fixed, offs in cases:
+            Hkv = H // 2
+            q = _bf16_values((H, L, d), rng, 1.5)
+            k = _bf16_values((Hkv, L, d), rng, 1.5)
+            scale = 0.37
+            mutant_caught = False
+            for h in range(H):
+                g = h // (H // Hkv)
+                kagg = orc.aggregate_keys(k[g], S, "none")
+                got = orc.stride_scores(q[h], kagg, S, h, scale, mode, layer, fixed)
+                want = _scores_from_token_matrix(q[h], k[g], S, offs[h], scale)
+                np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+                np.testing.assert_array_equal(np.isinf(got), np.isinf(want))
+                fin = np.isfinite(want)
+                np.testing.assert_allclose(got[fin], want[fin], rtol=0, atol=1e-12, err_msg=(mode, h, L))
+                if offs[h] != 0:
+                    bad = _mutant_stride_scores_without_offset(q[h], kagg, S, scale)
+                    ok = np.isfinite(want) & np.isfinite(bad)
+                    mutant_caught |= not np.allclose(bad[ok], want[ok], rtol=0, atol=1e-12)
+            if any(o != 0 for o in offs):
+                assert mutant_caught, (mode, L)
+
+
+@pytest.mark.parametrize("mode", ["head", "layer", "hybrid", "none"])
+def test_round_robin_block_scores_against_token_score_matrix(mode):
+    """The same pin through block_scores (the head index, its KV group and the
+    strategy reach the gather): softmax of the loop-built stride scores over
+    j <= i, summed per block cell and divided by r = Bk / S."""
+    S, H, Hkv, L, d, Bk = 4, 8, 2, 96, 8, 16
+    mode_, _, _, layer, fixed, offs = next(c for c in _golden_variant_rows()
+                                          if c[0] == mode and c[1] == H and c[2] == S)
+    rng = np.random.default_rng(61)
+    q = _bf16_values((1, H, L, d), rng, 2.0)
+    k = _bf16_values((1, Hkv, L, d), rng, 2.0)
+    prm = orc.Params(1, H, Hkv, L, d, S, Bk, 0.9, rr_mode=mode_, rr_layer=layer, rr_fixed=fixed)
+    m = orc.block_scores(q, k, prm, kagg_round="none")
+    r, ns, nb = Bk // S, L // S, L // Bk
+    for h in range(H):
+        s = _scores_from_token_matrix(q[0, h], k[0, h // (H // Hkv)], S, offs[h], prm.scale)
+        want = np.zeros((nb, nb))
+        for i in range(ns):
+            e = [math.exp(s[i, j] - max(s[i, :i + 1])) for j in range(i + 1)]
+            z = sum(e)
+            for j in range(i + 1):
+                want[i // r, j // r] += e[j] / z / r
+        np.testing.assert_allclose(m[0, h], want, rtol=0, atol=1e-13, err_msg=(mode, h))
 
 
 def test_aggregate_constant_stride_is_that_constant():
