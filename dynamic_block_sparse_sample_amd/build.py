@@ -20,7 +20,6 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librra.so")
-PROBE_LIB = os.path.join(PKG, "librra_probe.so")  # diagnostic: sustained MFMA rate and clock
 
 SOURCES = [
     "rra_validate.cpp",
@@ -33,7 +32,6 @@ SOURCES = [
     "kernels/xattn_scores.hip",
     "kernels/flash_attn.hip",
 ]
-PROBE_SOURCES = ["probe/mfma_rate.hip"]
 
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are disabled for all device code.
@@ -82,11 +80,10 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 1)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
-    _link(objs[: len(SOURCES)], LIB)
-    _link(objs[len(SOURCES):], PROBE_LIB)
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}")
     return LIB
 
 
