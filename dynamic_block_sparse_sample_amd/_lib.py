@@ -6,6 +6,7 @@ no fallback: if librra.so is missing or a call fails, an exception is raised.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -137,6 +138,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the binding allocates what a call needs (workspaces,
+    default outputs): the launch stream, so that torch's caching allocator
+    never hands those bytes to other work before the call's kernels finish."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -174,7 +182,8 @@ def _shapes(p: Params):
 def cast_f32_to_bf16(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     _need(src, "src", torch.float32, src.shape)
     if out is None:
-        out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
+        with _on(stream):
+            out = torch.empty(src.shape, dtype=torch.bfloat16, device=src.device)
     _need(out, "out", torch.bfloat16, src.shape)
     _check("rra_cast_f32_to_bf16", lib().rra_cast_f32_to_bf16(_ptr(src), _ptr(out), src.numel(), _stream(stream)))
     return out
@@ -184,7 +193,8 @@ def stride_aggregate(p: Params, k: torch.Tensor, kagg: torch.Tensor | None = Non
     _, kv, _, ns = _shapes(p)
     _need(k, "k", torch.bfloat16, kv)
     if kagg is None:
-        kagg = torch.empty((p.batch, p.num_kv_heads, ns, p.head_dim), dtype=torch.bfloat16, device=k.device)
+        with _on(stream):
+            kagg = torch.empty((p.batch, p.num_kv_heads, ns, p.head_dim), dtype=torch.bfloat16, device=k.device)
     _need(kagg, "kagg", torch.bfloat16, (p.batch, p.num_kv_heads, ns, p.head_dim))
     _check("rra_stride_aggregate", lib().rra_stride_aggregate(ctypes.byref(p), _ptr(k), _ptr(kagg), _stream(stream)))
     return kagg
@@ -196,7 +206,8 @@ def block_scores(p: Params, q: torch.Tensor, kagg: torch.Tensor, score: torch.Te
     _need(q, "q", torch.bfloat16, qs)
     _need(kagg, "kagg", torch.bfloat16, (p.batch, p.num_kv_heads, ns, p.head_dim))
     if score is None:
-        score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
     _need(score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
     _check("rra_block_scores",
            lib().rra_block_scores(ctypes.byref(p), _ptr(q), _ptr(kagg), _ptr(score), _stream(stream)))
@@ -210,7 +221,8 @@ def block_mass(p: Params, q: torch.Tensor, k: torch.Tensor, mass: torch.Tensor |
     _need(q, "q", torch.bfloat16, qs)
     _need(k, "k", torch.bfloat16, ks)
     if mass is None:
-        mass = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            mass = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
     _need(mass, "mass", torch.float32, (p.batch, p.num_heads, nb, nb))
     _check("rra_block_mass", lib().rra_block_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(mass), _stream(stream)))
     return mass
@@ -223,21 +235,23 @@ def xattn_block_scores(p: Params, q: torch.Tensor, k: torch.Tensor, score: torch
     _need(q, "q", torch.bfloat16, qs)
     _need(k, "k", torch.bfloat16, ks)
     if score is None:
-        score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
     _need(score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
     _check("rra_xattn_block_scores",
            lib().rra_xattn_block_scores(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(score), _stream(stream)))
     return score
 
 
-def _selection_buffers(p: Params, device, mask=None, idx=None, cnt=None):
+def _selection_buffers(p: Params, device, mask=None, idx=None, cnt=None, stream=None):
     _, _, nb, _ = _shapes(p)
-    if mask is None:
-        mask = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.uint8, device=device)
-    if idx is None:
-        idx = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.int32, device=device)
-    if cnt is None:
-        cnt = torch.empty((p.batch, p.num_heads, nb), dtype=torch.int32, device=device)
+    with _on(stream):
+        if mask is None:
+            mask = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.uint8, device=device)
+        if idx is None:
+            idx = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.int32, device=device)
+        if cnt is None:
+            cnt = torch.empty((p.batch, p.num_heads, nb), dtype=torch.int32, device=device)
     _need(mask, "mask", torch.uint8, (p.batch, p.num_heads, nb, nb))
     _need(idx, "idx", torch.int32, (p.batch, p.num_heads, nb, nb))
     _need(cnt, "cnt", torch.int32, (p.batch, p.num_heads, nb))
@@ -247,7 +261,7 @@ def _selection_buffers(p: Params, device, mask=None, idx=None, cnt=None):
 def top_tau(p: Params, score: torch.Tensor, mask=None, idx=None, cnt=None, stream=None):
     _, _, nb, _ = _shapes(p)
     _need(score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
-    mask, idx, cnt = _selection_buffers(p, score.device, mask, idx, cnt)
+    mask, idx, cnt = _selection_buffers(p, score.device, mask, idx, cnt, stream)
     _check("rra_top_tau", lib().rra_top_tau(ctypes.byref(p), _ptr(score), _ptr(mask), _ptr(idx), _ptr(cnt),
                                             _stream(stream)))
     return mask, idx, cnt
@@ -271,11 +285,13 @@ def estimate(p: Params, q: torch.Tensor, k: torch.Tensor, workspace: torch.Tenso
     _need(q, "q", torch.bfloat16, qs)
     _need(k, "k", torch.bfloat16, kv)
     if workspace is None:
-        workspace = alloc_workspace(p, q.device)
+        with _on(stream):
+            workspace = alloc_workspace(p, q.device)
     if out is None:
-        mask, idx, cnt = _selection_buffers(p, q.device)
-        score = (torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
-                 if return_score else None)
+        mask, idx, cnt = _selection_buffers(p, q.device, stream=stream)
+        with _on(stream):
+            score = (torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=q.device)
+                     if return_score else None)
         out = Selection(mask, idx, cnt, score)
     _selection_buffers(p, q.device, out.mask, out.idx, out.cnt)
     if out.score is not None:
@@ -293,7 +309,7 @@ def attn_workspace_size(p: Params) -> int:
     return int(n.value)
 
 
-def _attn_workspace(p: Params, device, workspace, schedule: str):
+def _attn_workspace(p: Params, device, workspace, schedule: str, stream=None):
     """(pointer, bytes) of the schedule workspace: a fresh one per call unless given
     (calls that may overlap need distinct ones); (None, 0) for schedule="static"."""
     if schedule == "static":
@@ -301,7 +317,8 @@ def _attn_workspace(p: Params, device, workspace, schedule: str):
     if schedule != "dynamic":
         raise ValueError(f"schedule must be 'dynamic' or 'static', not {schedule!r}")
     if workspace is None:
-        workspace = torch.empty(attn_workspace_size(p), dtype=torch.uint8, device=device)
+        with _on(stream):
+            workspace = torch.empty(attn_workspace_size(p), dtype=torch.uint8, device=device)
     return _ptr(workspace), _workspace_bytes(workspace, "workspace")
 
 
@@ -317,9 +334,10 @@ def sparse_attn(p: Params, q, k, v, idx, cnt, out=None, workspace=None, schedule
     _need(idx, "idx", torch.int32, (p.batch, p.num_heads, nb, nb))
     _need(cnt, "cnt", torch.int32, (p.batch, p.num_heads, nb))
     if out is None:
-        out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
+        with _on(stream):
+            out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, qs)
-    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule)
+    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule, stream)
     _check("rra_sparse_attn", lib().rra_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx),
                                                     _ptr(cnt), _ptr(out), ws, ws_bytes, _stream(stream)))
     return out
@@ -331,9 +349,10 @@ def dense_attn(p: Params, q, k, v, out=None, workspace=None, schedule="dynamic",
     _need(k, "k", torch.bfloat16, kv)
     _need(v, "v", torch.bfloat16, kv)
     if out is None:
-        out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
+        with _on(stream):
+            out = torch.empty(qs, dtype=torch.bfloat16, device=q.device)
     _need(out, "out", torch.bfloat16, qs)
-    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule)
+    ws, ws_bytes = _attn_workspace(p, q.device, workspace, schedule, stream)
     _check("rra_dense_attn", lib().rra_dense_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), ws,
                                                   ws_bytes, _stream(stream)))
     return out
