@@ -104,3 +104,59 @@ def check_output_rows(out_gpu, q, k, v, mask, prm: orc.Params, rows):
         got = to_f64(out_gpu[b, h, i * prm.block:(i + 1) * prm.block])
         worst = max(worst, out_err(got, ref))
     return worst
+
+
+REL_FLOOR = 1e-2  # relative errors are taken over output elements with |exact| >= this
+
+
+def output_errors(got: np.ndarray, ref: np.ndarray) -> dict:
+    """Error figures of bf16 outputs against the exact values: the bar's error
+    (beyond the output's own half-ulp rounding), the raw max-abs, and the max
+    relative error over elements whose exact value is at least REL_FLOOR."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    diff = np.abs(got - ref)
+    big = np.abs(ref) >= REL_FLOOR
+    return {"err": out_err(got, ref), "max_abs": float(diff.max()),
+            "max_rel": float((diff[big] / np.abs(ref[big])).max()) if big.any() else 0.0}
+
+
+def merge_errors(a: dict | None, b: dict) -> dict:
+    return dict(b) if a is None else {k: max(a[k], b[k]) for k in b}
+
+
+def seeded_rows(seed: int, batch: int, heads: int, nb: int, n: int = 64):
+    """n distinct seeded (b, h, query block) rows, always including the first
+    and the last query block."""
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, nb - 1), (batch - 1, heads - 1, 0)}
+    while len(rows) < min(n, batch * heads * nb):
+        rows.add((int(rng.integers(batch)), int(rng.integers(heads)), int(rng.integers(nb))))
+    return sorted(rows)
+
+
+def check_rows_by_head(out, q, k, v, mask, prm: orc.Params, rows) -> dict:
+    """Output rows against the oracle on the given mask, converting one head of
+    the CPU bf16 tensors q, k, v (torch) to float64 at a time, so that
+    full-size workloads need no float64 copy of the whole layer.  Returns the
+    merged output_errors of all rows."""
+    one = orc.Params(1, 1, 1, prm.seq_len, prm.head_dim, prm.stride, prm.block, prm.tau, prm.protect_last,
+                     prm.sm_scale, causal=prm.causal)
+    kv_cache = {}
+    res = None
+    by_head = {}
+    for (b, h, i) in rows:
+        by_head.setdefault((b, h), []).append(i)
+    for (b, h), blocks in sorted(by_head.items()):
+        g = h // prm.group
+        if (b, g) not in kv_cache:
+            kv_cache.clear()
+            kv_cache[(b, g)] = (to_f64(k[b:b + 1, g:g + 1]), to_f64(v[b:b + 1, g:g + 1]))
+        kh, vh = kv_cache[(b, g)]
+        qh = to_f64(q[b:b + 1, h:h + 1])
+        mh = np.asarray(mask[b:b + 1, h:h + 1])
+        for i in blocks:
+            ref = orc.attention_rows(qh, kh, vh, mh, one, 0, 0, i)
+            got = to_f64(out[b, h, i * prm.block:i * prm.block + ref.shape[0]])
+            res = merge_errors(res, output_errors(got, ref))
+    return res
