@@ -12,6 +12,7 @@ same library is timed on the same inputs for the speedup.
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload llama_128k]
+    python bench.py --mode workloads [--cpu-oracle]   # every configuration point
 """
 from __future__ import annotations
 
@@ -23,69 +24,222 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+# Exponential rate of the vector units: a wave-wide v_exp_f32 occupies its SIMD
+# for 8 cycles (half the full VALU rate; measured on this chip), so 256 CUs x
+# 4 SIMDs x 8 lanes per cycle x 2.4 GHz.
+PEAK_EXP_T_PER_S = 256 * 4 * 8 * 2.4e9 / 1e12
 COPY_BYTES = 256 << 20  # plain device copy used to calibrate the HBM byte counters
+FLUSH_BYTES = 512 << 20  # written between timed repetitions to evict L2 and the 256 MB memory-side cache
+FLUSH_MAX_L = 32768  # inputs of longer sequences exceed the caches by themselves
+TIE_TOL = 1e-4  # near-tie rule for masks (prefix within this of tau, or masses at the cut this close)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(q, k, v, sel_mask, cnt, w, f_dense, n_heads_sample=4, n_rows_sample=16):
-    """The fp64 CPU oracle on a bounded sample of the same workload.
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+class Timer:
+    """Per-repetition HIP-event timing on the current stream.  Between
+    repetitions, when asked, a 512 MB scratch buffer is written (outside the
+    timed events) so that no input stays cached from the previous one."""
 
-    Times the oracle's estimator on n_heads_sample query heads (full length)
-    and its attention on n_rows_sample sampled (head, query block) rows (on the
-    GPU's mask), then extrapolates to the whole layer: the estimator by head
-    count, the attention by the number of selected key blocks."""
+    def __init__(self, device, flush: bool):
+        import torch
+        self.torch = torch
+        self.scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=device) if flush else None
+
+    def reps(self, fn, reps: int, warmup: int):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            if self.scratch is not None:
+                self.scratch.fill_(1.0)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+
+def stats(ms):
+    v = sorted(ms)
+    return {"median": round(v[len(v) // 2], 4), "min": round(v[0], 4), "mean": round(sum(v) / len(v), 4),
+            "n": len(v)}
+
+
+# ---------------------------------------------------------------------------
+# Roofline fractions
+# ---------------------------------------------------------------------------
+def estimator_fracs(p, sum_cnt: int, t_est_ms: float, t_agg_ms: float) -> dict:
+    """Roofline fractions of the estimator and of its aggregation kernel, by
+    the method's algorithmic work (single pass; the kernel's recompute is not
+    counted):
+
+      bytes = K read once + the sampled queries + mask, index lists and counts
+              written (Kagg and block scores are intermediates);
+      flops = 2 d Bz H Ns (Ns + 1) / 2 (each sampled query against its visible
+              strides), exps = Bz H Ns (Ns + 1) / 2;
+      binding fraction = max(bytes / BW, flops / P_bf16, exps / R_exp) / t.
+
+    The two-pass kernel executes twice the flops and exps; that figure is
+    reported apart.  Aggregation: K read + Kagg written over its own time."""
+    L, d, nb, ns = p.seq_len, p.head_dim, p.num_blocks, p.num_strides
+    k_bytes = p.batch * p.num_kv_heads * L * d * 2
+    kagg_b = p.batch * p.num_kv_heads * ns * d * 2
+    est_bytes = (k_bytes + p.batch * p.num_heads * ns * d * 2 + p.batch * p.num_heads * nb * nb
+                 + 4 * sum_cnt + 4 * p.batch * p.num_heads * nb)
+    pairs = p.batch * p.num_heads * ns * (ns + 1) / 2 if p.causal else p.batch * p.num_heads * ns * ns
+    flops, exps = 2.0 * d * pairs, pairs
+    floors = {"hbm": est_bytes / (PEAK_HBM_GBS * 1e9), "mfma": flops / (PEAK_BF16_TFLOPS * 1e12),
+              "exp": exps / (PEAK_EXP_T_PER_S * 1e12)}
+    bound = max(floors, key=floors.get)
+    t = t_est_ms * 1e-3
+    return {
+        "estimator_algorithmic": {"bytes": est_bytes, "flops": flops, "exps": exps,
+                                  "floor_us": {kk: round(vv * 1e6, 2) for kk, vv in floors.items()},
+                                  "bound": bound},
+        "estimator_hbm_frac": round(est_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
+        "estimator_binding_roofline_frac": round(floors[bound] / t, 4),
+        "estimator_executed_two_pass_mfma_frac": round(2 * flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (t_agg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg: timing, and the parity figures of the same calls
+# ---------------------------------------------------------------------------
+def _row_order(vals):
     import numpy as np
-    import torch
+    return np.lexsort((np.arange(vals.size), -vals))
+
+
+def _classify_row(gsel, osel, vals, tau):
+    """'equal', 'near_tie' (differs where an oracle prefix lies within TIE_TOL
+    of tau or the masses at the cut are that close) or 'other'."""
+    import numpy as np
+    if np.array_equal(gsel, osel):
+        return "equal"
+    T = vals.sum()
+    if not T > 0:
+        return "other"
+    order = _row_order(vals)
+    csum = np.cumsum(vals[order]) / T
+    ks = osel.size
+    prefix = np.any(np.abs(csum - tau) < TIE_TOL)
+    cut = ks < vals.size and abs(vals[order[ks - 1]] - vals[order[ks]]) < TIE_TOL * vals[order[ks - 1]]
+    return "near_tie" if (prefix or cut) else "other"
+
+
+def _bf16_out_errors(got, ref):
+    import numpy as np
+    diff = np.abs(got - ref)
+    _, ex = np.frexp(np.abs(ref))
+    half_ulp = np.ldexp(1.0, np.maximum(ex - 1, -126) - 8)
+    big = np.abs(ref) >= 1e-2
+    return {"err": float(np.max(diff - half_ulp)), "max_abs": float(diff.max()),
+            "max_rel": float((diff[big] / np.abs(ref[big])).max()) if big.any() else 0.0}
+
+
+def cpu_baseline(w, S, tau, q, k, v, gpu_mask, gpu_cnt, out, f_dense, t_gpu_ms, est_heads=None, n_rows=64,
+                 full_attention=False, seed=0) -> dict:
+    """The float64 CPU oracle, as it stands, on the same inputs, timed on this
+    host with its BLAS limited to the cores this process may run on.
+
+    Estimator: est_heads query heads at full length (None: every head), each
+    KV group's aggregation once.  Attention: every row when full_attention,
+    else n_rows seeded (head, query block) rows on the GPU's mask,
+    extrapolated to the layer by selected key blocks.  Untimed, the same
+    calls give the parity figures of the run: the timed heads' mask rows
+    against the GPU's (equal / near-tie / other) and the attention rows'
+    errors against the GPU's output (beyond half a bf16 ulp, raw max-abs, max
+    relative over |exact| >= 1e-2).  q, k, v are host bf16 tensors."""
+    import numpy as np
+    import threadpoolctl
     from oracle import rra_oracle as orc
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        cores = max([d.get("num_threads", 1) for d in info] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    prm = orc.Params(w.batch, w.num_heads, w.num_kv_heads, w.seq_len, w.head_dim, w.stride, w.block,
-                     float(np.float32(w.tau)), True)
-    nb = prm.num_blocks
-    t0 = time.perf_counter()
-    for h in range(n_heads_sample):
-        g = h // prm.group
-        kagg = orc.aggregate_keys(k[0, g].double().numpy(), prm.stride)
-        s = orc.stride_scores(q[0, h].double().numpy(), kagg, prm.stride, h, prm.scale)
-        m = orc.pool_blocks(orc.stride_softmax(s), prm.strides_per_block)
-        for i in range(nb):
-            orc.top_tau_row(m[i], i, prm.tau, i == nb - 1)
-    t_est = (time.perf_counter() - t0) / n_heads_sample * w.num_heads * w.batch
-    rng = np.random.default_rng(0)
-    rows = [(0, int(rng.integers(0, w.num_heads)), int(rng.integers(nb // 2, nb))) for _ in range(n_rows_sample)]
-    t_attn_sample = 0.0
-    blocks_sample = 0
-    for (b, h, i) in rows:
-        g = h // prm.group
-        sub_q = q[b:b + 1, h:h + 1].double().numpy()
-        sub_k = k[b:b + 1, g:g + 1].double().numpy()
-        sub_v = v[b:b + 1, g:g + 1].double().numpy()
-        one = orc.Params(1, 1, 1, prm.seq_len, prm.head_dim, prm.stride, prm.block, prm.tau, True)
-        mrow = sel_mask[b:b + 1, h:h + 1]
-        t1 = time.perf_counter()
-        orc.attention_rows(sub_q, sub_k, sub_v, mrow, one, 0, 0, i)
-        t_attn_sample += time.perf_counter() - t1
-        blocks_sample += int(cnt[b, h, i])
-    t_attn = t_attn_sample / max(blocks_sample, 1) * float(cnt.sum())
-    t_total = t_est + t_attn
+
+    cores = len(os.sched_getaffinity(0))
+    H, B = w.num_heads, w.batch
+    prm = orc.Params(B, H, w.num_kv_heads, w.seq_len, w.head_dim, S, w.block, float(np.float32(tau)), True)
+    nb, G = prm.num_blocks, prm.group
+    heads = list(range(H)) if est_heads is None else list(est_heads)
+    f64 = lambda t: t.to(dtype=__import__("torch").float64).numpy()  # noqa: E731
+    rows_cls = {"equal": 0, "near_tie": 0, "other": 0}
+    t_est = 0.0
+    t_wall0 = time.perf_counter()
+    with threadpoolctl.threadpool_limits(cores):
+        for b in range(B):
+            kagg_g = None
+            for h in heads:
+                g = h // G
+                if kagg_g is None or kagg_g[0] != g:
+                    kg = f64(k[b, g])
+                    t0 = time.perf_counter()
+                    kagg_g = (g, orc.aggregate_keys(kg, S))
+                    t_est += time.perf_counter() - t0
+                qh = f64(q[b, h])
+                t0 = time.perf_counter()
+                s = orc.stride_scores(qh, kagg_g[1], S, h, prm.scale)
+                m = orc.pool_blocks(orc.stride_softmax(s), prm.strides_per_block)
+                sels = [orc.top_tau_row(m[i], i, prm.tau, i == nb - 1) for i in range(nb)]
+                t_est += time.perf_counter() - t0
+                for i in range(nb):
+                    gsel = np.nonzero(gpu_mask[b, h, i, :i + 1])[0]
+                    rows_cls[_classify_row(gsel, sels[i], m[i, :i + 1], prm.tau)] += 1
+        t_est_layer = t_est * (H / len(heads))
+        if full_attention:
+            rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(nb)]
+        else:
+            rng = np.random.default_rng(seed)
+            rows = sorted({(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(nb)))
+                           for _ in range(4 * n_rows)})
+            rng.shuffle(rows)
+            rows = sorted(rows[:n_rows])
+        one = orc.Params(1, 1, 1, prm.seq_len, prm.head_dim, S, prm.block, prm.tau, True)
+        t_attn, blocks, errs, cur = 0.0, 0, None, None
+        for (b, h, i) in rows:
+            if cur != (b, h):
+                cur = (b, h)
+                g = h // G
+                qh, kh, vh = f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, g:g + 1]), f64(v[b:b + 1, g:g + 1])
+                mh = gpu_mask[b:b + 1, h:h + 1]
+            t0 = time.perf_counter()
+            ref = orc.attention_rows(qh, kh, vh, mh, one, 0, 0, i)
+            t_attn += time.perf_counter() - t0
+            blocks += int(gpu_cnt[b, h, i])
+            got = f64(out[b, h, i * prm.block:i * prm.block + ref.shape[0]].cpu())
+            e = _bf16_out_errors(got, ref)
+            errs = e if errs is None else {kk: max(errs[kk], e[kk]) for kk in e}
+        t_attn_layer = t_attn if full_attention else t_attn / max(blocks, 1) * float(gpu_cnt.sum())
+    t_total = t_est_layer + t_attn_layer
+    extrapolated = est_heads is not None or not full_attention
     return {
         "value": f_dense / t_total / 1e12,
-        "unit": "TFLOP/s",
-        "cores": int(cores),
+        "unit": "TFLOP/s (dense-equivalent causal attention FLOPs / oracle step time)",
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: estimator on {n_heads_sample} of {w.num_heads} heads at full length "
-                   f"({time.perf_counter() - t0:.1f} s wall incl. attention), attention on {n_rows_sample} sampled "
-                   f"(head, query-block) rows ({blocks_sample} key blocks); extrapolated to the whole layer "
-                   f"by heads and by selected blocks: {t_total:.0f} s per step"),
-        "extrapolated_s_per_step": t_total,
+        "sample": (f"fp64 numpy oracle, BLAS limited to {cores} threads (elementwise steps single-threaded): "
+                   f"estimator on {len(heads)} of {H} heads at full length ({t_est:.1f} s), attention on "
+                   + ("every row" if full_attention else f"{len(rows)} seeded (head, query block) rows")
+                   + f" ({blocks} key blocks, {t_attn:.1f} s)"
+                   + ("; extrapolated to the layer by heads and by selected key blocks" if extrapolated else "")
+                   + f": {t_total:.1f} s per step"),
+        "extrapolated": extrapolated,
+        "s_per_step": t_total,
+        "estimate_s": t_est_layer,
+        "sparse_attn_s": t_attn_layer,
+        "gpu_over_cpu": t_total / (t_gpu_ms * 1e-3),
+        "wall_s": time.perf_counter() - t_wall0,
         "cpu_model": _cpu_model(),
+        "parity": {"mask_rows_compared": sum(rows_cls.values()), **{f"mask_rows_{kk}": vv for kk, vv in
+                                                                   rows_cls.items()},
+                   "output_rows_compared": len(rows), "output_err_beyond_half_ulp": errs["err"],
+                   "output_max_abs": errs["max_abs"], "output_max_rel": errs["max_rel"]},
     }
 
 
@@ -99,6 +253,17 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _round_floats(d):
+    if isinstance(d, dict):
+        return {kk: _round_floats(vv) for kk, vv in d.items()}
+    if isinstance(d, float):
+        return float(f"{d:.6g}")
+    return d
+
+
+# ---------------------------------------------------------------------------
+# Headline step
+# ---------------------------------------------------------------------------
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,16 +271,21 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=20, help="timed repetitions per point (workloads mode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-oracle", action="store_true",
+                    help="workloads mode: also time the CPU oracle per point (estimator over every head; "
+                         "attention in full at 1K and 8K, else 64 seeded rows) with its parity figures")
     ap.add_argument("--mode", choices=["bench", "profile", "power", "selection", "workloads"], default="bench",
                     help="profile: one estimate, --steps sparse-attention launches, one dense launch and a "
                          "256 MiB device copy (HBM-counter calibration); prints a short summary only. "
-                         "power: socket power (amd-smi) while sparse attention, dense attention and the "
-                         "MFMA probe each run back to back for --power-secs seconds. "
+                         "power: socket power (amd-smi) while sparse and dense attention each run back to "
+                         "back for --power-secs seconds. "
                          "selection: precision / recall / F1 and kept attention mass of the estimated "
                          "selections (round-robin variants, several S and tau) against the exact Top-tau "
-                         "selection, one JSON line per point. workloads: estimate / sparse / dense times and "
-                         "density of every bf16 workload at its own settings, one JSON line each")
+                         "selection, one JSON line per point. workloads: estimate / sparse / dense times "
+                         "(median and min of --reps, caches flushed between repetitions up to 32K) and "
+                         "density of every workload at its own settings, one JSON line each")
     ap.add_argument("--power-secs", type=float, default=6.0)
     ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "profiles", "traffic_sparse_attn_llama_128k.json"))
@@ -139,7 +309,7 @@ def main(argv=None) -> int:
             print(json.dumps(line), flush=True)
         return 0
     if args.mode == "workloads":
-        for line in workloads_report():
+        for line in workloads_report(args.reps, args.cpu_oracle):
             print(json.dumps(line), flush=True)
         return 0
     w = wl.WORKLOADS[args.workload]
@@ -209,40 +379,29 @@ def main(argv=None) -> int:
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    sp_times = sorted(a.elapsed_time(b) for a, b in sp_ev)
+    sp_times = [a.elapsed_time(b) for a, b in sp_ev]
+    est_times = [a.elapsed_time(b) for a, b in est_ev]
     t_sp = sum(sp_times) / args.steps
-    t_est = sum(a.elapsed_time(b) for a, b in est_ev) / args.steps
+    t_est = sum(est_times) / args.steps
+    log(f"[bench] {ms_step:.3f} ms per step (estimate {t_est:.3f}, sparse attention {t_sp:.3f})")
 
     # per-kernel breakdown of the estimator (same buffers)
     kagg = ws[: p.batch * p.num_kv_heads * p.num_strides * p.head_dim * 2].view(torch.bfloat16).view(
         p.batch, p.num_kv_heads, p.num_strides, p.head_dim)
     score = torch.empty((p.batch, p.num_heads, nb, nb), dtype=torch.float32, device=dev)
-    reps = 5
+    timer = Timer(dev, flush=w.seq_len <= FLUSH_MAX_L)
     brk = {}
     for name, fn in [("stride_aggregate", lambda: rra.stride_aggregate(p, kd, kagg)),
                      ("block_scores", lambda: rra.block_scores(p, qd, kagg, score)),
                      ("top_tau", lambda: rra.top_tau(p, score, sel.mask, sel.idx, sel.cnt))]:
-        fn()
-        a, b = E(), E()
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        brk[name] = a.elapsed_time(b) / reps
+        brk[name] = stats(timer.reps(fn, 5, 1))
+    del score
 
     log(f"[bench] dense baseline x{args.dense_reps}")
-    rra.dense_attn(p, qd, kd, vd, out=dense_out)
-    torch.cuda.synchronize()
-    a, b = E(), E()
-    a.record()
-    for _ in range(args.dense_reps):
-        rra.dense_attn(p, qd, kd, vd, out=dense_out)
-    b.record()
-    torch.cuda.synchronize()
-    t_dense = a.elapsed_time(b) / args.dense_reps
+    dn_times = timer.reps(lambda: rra.dense_attn(p, qd, kd, vd, out=dense_out), args.dense_reps, 1)
+    t_dense = sum(dn_times) / len(dn_times)
 
-    # the timed steps left the selection of this input in sel
+    # the timed steps left the selection and output of this input in sel / out
     cnt = sel.cnt.cpu()
     sum_cnt = int(cnt.sum())
     causal_blocks = p.batch * p.num_heads * nb * (nb + 1) // 2
@@ -285,17 +444,19 @@ def main(argv=None) -> int:
         "t_estimate_ms": round(t_est, 4),
         "t_sparse_attn_ms": round(t_sp, 4),
         "t_dense_attn_ms": round(t_dense, 4),
+        "t_estimate_ms_stats": stats(est_times),
+        "t_sparse_attn_ms_stats": stats(sp_times),
+        "t_dense_attn_ms_stats": stats(dn_times),
         "speedup_vs_dense": round(t_dense / ms_step, 4),
         "mask_density": round(density, 5),
         "mask_density_per_head": {"min": round(float(per_head[0]), 5),
                                   "median": round(float(per_head[len(per_head) // 2]), 5),
                                   "max": round(float(per_head[-1]), 5)},
         "mask_density_without_protected_row": round(dens_no_last, 5),
-        "t_sparse_attn_ms_median_min": [round(sp_times[len(sp_times) // 2], 4), round(sp_times[0], 4)],
         "sparse_attn_unmasked_tflops": round(
             (f_sel - 4.0 * d * diag_sel * (Bk * Bk - Bk * (Bk + 1) / 2)) / (t_sp * 1e-3) / 1e12, 2),
-        "estimator_kernels_ms": {kk: round(vv, 4) for kk, vv in brk.items()},
-        **estimator_fracs(p, sum_cnt, t_est, brk["stride_aggregate"]),
+        "estimator_kernels_ms": brk,
+        **estimator_fracs(p, sum_cnt, t_est, brk["stride_aggregate"]["median"]),
         "dense_attn_tflops": round(f_dense / (t_dense * 1e-3) / 1e12, 2),
         "roofline": {"kernel": "flash_attn_kernel<128,128> (rra_sparse_attn)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -303,117 +464,48 @@ def main(argv=None) -> int:
                      "flops_per_launch": f_sel, "avg_launch_ms": round(t_sp, 4)},
     }
     line["pattern_search_vs_xattn"] = pattern_search_comparison(w, qd, kd)
-    ceil = mfma_ceiling()
-    if ceil is not None:
-        ceil["sparse_attn_frac_of_random_operand_rate"] = round(achieved / ceil["random_operands"]["tflops"], 4)
-    line["mfma_sustained"] = ceil
     if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline (bounded sample)")
-        cb = cpu_baseline(q, k, v, sel.mask.cpu().numpy(), cnt.numpy(), w, f_dense)
-        line["cpu_baseline"] = {kk: (round(vv, 6) if isinstance(vv, float) else vv) for kk, vv in cb.items()}
+        log("[bench] CPU oracle baseline (bounded sample: 4 heads' estimator, 64 attention rows)")
+        cb = cpu_baseline(w, w.stride, w.tau, q, k, v, sel.mask.cpu().numpy(), cnt.numpy(), out, f_dense, ms_step,
+                          est_heads=[0, 9, 18, 27] if w.num_heads >= 28 else None, n_rows=64, seed=0)
+        line["cpu_baseline"] = _round_floats(cb)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
     return 0
 
 
-def mfma_ceiling() -> dict | None:
-    """Sustained bf16 MFMA rate and shader clock of a pure matrix-core loop
-    (librra_probe.so), with zero and with random N(0,1) operands."""
-    import ctypes
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd",
-                        "librra_probe.so")
-    if not os.path.exists(path):
-        return None
-    lib = ctypes.CDLL(path)
-    fn = lib.rra_probe_mfma_rate
-    fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
-    res = {}
-    for name, operands in (("zero_operands", 0), ("random_operands", 1)):
-        # ~0.5 s of warm-up lets the clock settle after the attention runs (the
-        # power manager reacts over tens of ms); then the median of 3 runs of ~60 ms
-        runs = []
-        t0 = time.time()
-        while True:
-            tf, ghz = ctypes.c_double(0.0), ctypes.c_double(0.0)
-            rc = fn(operands, 200000, ctypes.byref(tf), ctypes.byref(ghz))
-            if rc != 0:
-                log(f"[bench] MFMA probe failed with HIP error {rc}")
-                return None
-            if time.time() - t0 > 0.5:
-                runs.append((tf.value, ghz.value))
-            if len(runs) == 3:
-                break
-        runs.sort()
-        res[name] = {"tflops": round(runs[1][0], 1), "clock_ghz": round(runs[1][1], 3)}
-    return res
-
-
-SELECTION_POINTS = {
-    "llama_8k": [(16, 0.9)],
-    "llama_32k": [(s, t) for s in (8, 16, 32) for t in (0.8, 0.9, 0.95)],
-    "video_64k": [(16, 0.95)],
-    "llama_128k": [(16, 0.9)],
-}
-
-
-def estimator_fracs(p, sum_cnt: int, t_est_ms: float, t_agg_ms: float) -> dict:
-    """Roofline fractions of the estimator and of its aggregation kernel.
-
-    Algorithmic bytes of the estimator: K read once, the sampled queries, the
-    mask, index lists and counts written (Kagg and block-score round trips are
-    intermediates).  Binding roofline: max(bytes / BW, executed flops / P_bf16)
-    / t, the two-pass scores executing 2 * 2d * Bz * H * Ns (Ns + 1) / 2 flops.
-    Aggregation: K read + Kagg written over its own time."""
-    L, d, nb, ns = p.seq_len, p.head_dim, p.num_blocks, p.num_strides
-    k_bytes = p.batch * p.num_kv_heads * L * d * 2
-    kagg_b = p.batch * p.num_kv_heads * ns * d * 2
-    est_bytes = (k_bytes + p.batch * p.num_heads * ns * d * 2 + p.batch * p.num_heads * nb * nb
-                 + 4 * sum_cnt + 4 * p.batch * p.num_heads * nb)
-    flops2 = 2 * 2.0 * d * p.batch * p.num_heads * ns * (ns + 1) / 2
-    return {
-        "estimator_hbm_frac": round(est_bytes / (t_est_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "estimator_binding_roofline_frac": round(
-            max(est_bytes / (PEAK_HBM_GBS * 1e9), flops2 / (PEAK_BF16_TFLOPS * 1e12)) / (t_est_ms * 1e-3), 4),
-        "stride_aggregate_hbm_frac": round((k_bytes + kagg_b) / (t_agg_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-    }
-
-
-def workloads_report(reps=5):
+# ---------------------------------------------------------------------------
+# Every configuration point
+# ---------------------------------------------------------------------------
+def workloads_report(reps=20, cpu_oracle=False):
     """Every configuration point at its own settings: the five workloads, and
     the 32K one swept over S in {8, 16, 32} x tau in {0.8, 0.9, 0.95}.  Per
     point: the estimator and its aggregation kernel, sparse and dense attention
-    (event-timed averages of `reps` launches), density, TFLOP/s and roofline
-    fractions.  fp32 workloads are cast to bf16 on the GPU first (timed apart)."""
+    (median and min of `reps` event-timed launches after 5 warm-ups, a 512 MB
+    scratch write between launches up to 32K), density, TFLOP/s and roofline
+    fractions; with cpu_oracle, the CPU oracle's time for the point and its
+    parity figures.  fp32 workloads are cast to bf16 on the GPU first (timed
+    apart)."""
     import torch
 
     import dynamic_block_sparse_sample_amd as rra
     from dynamic_block_sparse_sample_amd import workloads as wl
 
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
     for name, w in wl.WORKLOADS.items():
         log(f"[workloads] {name}")
         q, k, v = wl.make_inputs(w)
+        timer = Timer("cuda", flush=w.seq_len <= FLUSH_MAX_L)
         t_cast = None
         if w.fp32_inputs:
             q32, k32, v32 = q.cuda(), k.cuda(), v.cuda()
             qd, kd, vd = (torch.empty(t.shape, dtype=torch.bfloat16, device="cuda") for t in (q32, k32, v32))
-            t_cast = timed(lambda: [rra.cast_f32_to_bf16(s_, d_) for s_, d_ in ((q32, qd), (k32, kd), (v32, vd))])
+            t_cast = stats(timer.reps(lambda: [rra.cast_f32_to_bf16(s_, d_) for s_, d_ in
+                                               ((q32, qd), (k32, kd), (v32, vd))], reps, 5))
             del q32, k32, v32
+            q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))  # what the GPU computes on (RNE, as the cast)
         else:
             qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-        del q, k, v
         sweep = [(S, tau) for S in (8, 16, 32) for tau in (0.8, 0.9, 0.95)] if name == "llama_32k" else [
             (w.stride, w.tau)]
         out = torch.empty_like(qd)
@@ -424,34 +516,111 @@ def workloads_report(reps=5):
             sel = rra.Selection(*rra._lib._selection_buffers(p, qd.device), None)
             kagg = torch.empty((p.batch, p.num_kv_heads, p.num_strides, p.head_dim), dtype=torch.bfloat16,
                                device=qd.device)
-            t_est = timed(lambda: rra.estimate(p, qd, kd, workspace=ws, out=sel))
-            t_agg = timed(lambda: rra.stride_aggregate(p, kd, kagg))
-            t_sp = timed(lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out))
+            t_est = stats(timer.reps(lambda: rra.estimate(p, qd, kd, workspace=ws, out=sel), reps, 5))
+            t_agg = stats(timer.reps(lambda: rra.stride_aggregate(p, kd, kagg), reps, 5))
+            t_sp = stats(timer.reps(lambda: rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out), reps, 5))
             if t_dense is None:  # depends on the shape only
-                t_dense = timed(lambda: rra.dense_attn(p, qd, kd, vd, out=out))
+                t_dense = stats(timer.reps(lambda: rra.dense_attn(p, qd, kd, vd, out=out), max(reps // 2, 3), 2))
+            rra.sparse_attn(p, qd, kd, vd, sel.idx, sel.cnt, out=out)
+            torch.cuda.synchronize()
             nb = p.num_blocks
             sum_cnt = int(sel.cnt.sum())
             f_sel = 4.0 * w.head_dim * w.block * w.block * sum_cnt
             f_full = 4.0 * w.head_dim * w.block * w.block * w.batch * w.num_heads * nb * (nb + 1) / 2
             f_dense = 4.0 * w.head_dim * w.batch * w.num_heads * w.seq_len * (w.seq_len + 1) / 2
+            te, ts, td = t_est["median"], t_sp["median"], t_dense["median"]
             line = {"mode": "workloads", "workload": name, "seq_len": w.seq_len,
                     "heads": f"{w.num_heads}/{w.num_kv_heads}", "head_dim": w.head_dim, "block": w.block,
-                    "stride": S, "tau": tau,
+                    "stride": S, "tau": tau, "caches_flushed": timer.scratch is not None,
                     "density": round(sum_cnt / (w.batch * w.num_heads * nb * (nb + 1) / 2), 4),
-                    "t_estimate_ms": round(t_est, 4), "t_stride_aggregate_ms": round(t_agg, 4),
-                    "t_sparse_attn_ms": round(t_sp, 4), "t_dense_attn_ms": round(t_dense, 4),
-                    "sparse_tflops": round(f_sel / (t_sp * 1e-3) / 1e12, 1),
-                    "sparse_mfma_frac": round(f_sel / (t_sp * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                    "dense_tflops": round(f_full / (t_dense * 1e-3) / 1e12, 1),
-                    "effective_tflops": round(f_dense / ((t_est + t_sp) * 1e-3) / 1e12, 1),
-                    "speedup_vs_dense": round(t_dense / (t_est + t_sp), 3),
-                    **estimator_fracs(p, sum_cnt, t_est, t_agg)}
+                    "t_estimate_ms": t_est, "t_stride_aggregate_ms": t_agg,
+                    "t_sparse_attn_ms": t_sp, "t_dense_attn_ms": t_dense,
+                    "sparse_tflops": round(f_sel / (ts * 1e-3) / 1e12, 1),
+                    "sparse_mfma_frac": round(f_sel / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                    "dense_tflops": round(f_full / (td * 1e-3) / 1e12, 1),
+                    "effective_tflops": round(f_dense / ((te + ts) * 1e-3) / 1e12, 1),
+                    "speedup_vs_dense": round(td / (te + ts), 3),
+                    **estimator_fracs(p, sum_cnt, te, t_agg["median"])}
             if t_cast is not None:
-                line["t_cast_f32_to_bf16_ms"] = round(t_cast, 4)
+                line["t_cast_f32_to_bf16_ms"] = t_cast
+            if cpu_oracle:
+                log(f"[workloads] {name} S={S} tau={tau}: CPU oracle")
+                full_attn = w.seq_len <= 8192
+                cb = cpu_baseline(w, S, tau, q, k, v, sel.mask.cpu().numpy(), sel.cnt.cpu().numpy(), out,
+                                  f_dense, te + ts, est_heads=None, n_rows=64, full_attention=full_attn, seed=S)
+                line["cpu_oracle"] = _round_floats(cb)
+            log(f"[workloads] {name} S={S} tau={tau}: sparse {ts:.3f} ms, dense {td:.3f} ms, "
+                f"estimate {te:.3f} ms, density {line['density']}")
             yield line
             del ws, sel, kagg
-        del qd, kd, vd, out
+        del qd, kd, vd, out, timer
         torch.cuda.empty_cache()
+
+
+def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
+    """Median socket power (amd-smi, sampled from a thread) while each workload
+    runs back to back, its rate, and the energy per flop above idle."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run(["amd-smi", "metric", "--power"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
+                if m:
+                    samples.append((time.time(), float(m.group(1))))
+            except Exception:
+                pass
+            time.sleep(0.1)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    phases = []
+    time.sleep(2.0)
+    phases.append(("idle", time.time() - 2.0, time.time(), None))
+    for name, fn, flops in (("sparse_attn", sparse_fn, f_sparse), ("dense_attn", dense_fn, f_dense)):
+        fn()
+        torch.cuda.synchronize()
+        t0, n = time.time(), 0
+        while time.time() - t0 < secs:
+            fn()
+            torch.cuda.synchronize()
+            n += 1
+        t1 = time.time()
+        phases.append((name, t0, t1, flops * n / (t1 - t0) / 1e12))
+        log(f"[bench] power phase {name}: {n} runs")
+        time.sleep(1.5)
+    stop.set()
+    th.join(timeout=15)
+    res = {"mode": "power", "samples": len(samples), "phases": {}}
+    idle_w = None
+    for name, t0, t1, rate in phases:
+        vals = sorted(wt for ts, wt in samples if t0 + 0.8 < ts < t1 - 0.2)
+        med = vals[len(vals) // 2] if vals else None
+        if name == "idle":
+            idle_w = med
+        entry = {"median_w": med, "n_samples": len(vals)}
+        if rate is not None:
+            entry["tflops"] = round(rate, 1)
+            if med is not None and idle_w is not None:
+                entry["pj_per_flop_above_idle"] = round((med - idle_w) / (rate * 1e12) * 1e12, 3)
+        res["phases"][name] = entry
+    return res
+
+
+SELECTION_POINTS = {
+    "llama_8k": [(16, 0.9)],
+    "llama_32k": [(s, t) for s in (8, 16, 32) for t in (0.8, 0.9, 0.95)],
+    "video_64k": [(16, 0.95)],
+    "llama_128k": [(16, 0.9)],
+}
 
 
 def xattn_supported(p) -> bool:
@@ -579,82 +748,6 @@ def selection_report(first_workload: str):
         torch.cuda.empty_cache()
 
 
-def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
-    """Median socket power (amd-smi, sampled from a thread) while each workload
-    runs back to back, its rate, and the energy per flop above idle."""
-    import ctypes
-    import re
-    import subprocess
-    import threading
-
-    import torch
-
-    samples, stop = [], threading.Event()
-
-    def sampler():
-        while not stop.is_set():
-            try:
-                txt = subprocess.run(["amd-smi", "metric", "--power"], capture_output=True, text=True,
-                                     timeout=10).stdout
-                m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", txt)
-                if m:
-                    samples.append((time.time(), float(m.group(1))))
-            except Exception:
-                pass
-            time.sleep(0.1)
-
-    probe_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd",
-                              "librra_probe.so")
-    probe = ctypes.CDLL(probe_path).rra_probe_mfma_rate
-    probe.restype = ctypes.c_int
-    probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
-    last = {}
-
-    def mfma(operands):
-        tf, ghz = ctypes.c_double(), ctypes.c_double()
-        assert probe(operands, 200000, ctypes.byref(tf), ctypes.byref(ghz)) == 0
-        last["tflops"], last["clock_ghz"] = tf.value, ghz.value
-
-    th = threading.Thread(target=sampler, daemon=True)
-    th.start()
-    phases = []
-    time.sleep(2.0)
-    phases.append(("idle", time.time() - 2.0, time.time(), None, None))
-    for name, fn, flops in (("sparse_attn", sparse_fn, f_sparse), ("dense_attn", dense_fn, f_dense),
-                            ("mfma_probe_random_operands", lambda: mfma(1), None),
-                            ("mfma_probe_zero_operands", lambda: mfma(0), None)):
-        fn()
-        torch.cuda.synchronize()
-        t0, n = time.time(), 0
-        while time.time() - t0 < secs:
-            fn()
-            torch.cuda.synchronize()
-            n += 1
-        t1 = time.time()
-        rate = flops * n / (t1 - t0) / 1e12 if flops else last["tflops"]
-        phases.append((name, t0, t1, rate, None if flops else last["clock_ghz"]))
-        log(f"[bench] power phase {name}: {n} runs")
-        time.sleep(1.5)
-    stop.set()
-    th.join(timeout=15)
-    res = {"mode": "power", "samples": len(samples), "phases": {}}
-    idle_w = None
-    for name, t0, t1, rate, ghz in phases:
-        v = sorted(wt for ts, wt in samples if t0 + 0.8 < ts < t1 - 0.2)
-        med = v[len(v) // 2] if v else None
-        if name == "idle":
-            idle_w = med
-        entry = {"median_w": med, "n_samples": len(v)}
-        if rate is not None:
-            entry["tflops"] = round(rate, 1)
-            if med is not None and idle_w is not None:
-                entry["pj_per_flop_above_idle"] = round((med - idle_w) / (rate * 1e12) * 1e12, 3)
-        if ghz is not None:
-            entry["clock_ghz"] = round(ghz, 3)
-        res["phases"][name] = entry
-    return res
-
-
 def _kernel_hash() -> str:
     """Hash of the attention kernel source (flash_attn.hip and its work-order
     header fa_order.h); traffic counters are only valid for it."""
@@ -666,6 +759,7 @@ def _kernel_hash() -> str:
         with open(os.path.join(kdir, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
 
 
 if __name__ == "__main__":
