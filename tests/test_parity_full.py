@@ -190,7 +190,9 @@ def llama_128k():
     score = torch.empty((1, p.num_heads, p.num_blocks, p.num_blocks), dtype=torch.float32, device=qd.device)
     sel2 = rra.estimate(p, qd, kd, out=rra.Selection(*rra._lib._selection_buffers(p, qd.device), score))
     torch.cuda.synchronize()
-    assert torch.equal(sel.mask, sel2.mask) and torch.equal(sel.cnt, sel2.cnt) and torch.equal(sel.idx, sel2.idx)
+    assert torch.equal(sel.mask, sel2.mask) and torch.equal(sel.cnt, sel2.cnt)
+    listed = torch.arange(p.num_blocks, device=qd.device) < sel.cnt.unsqueeze(-1)  # entries past cnt are unwritten
+    assert torch.equal(sel.idx[listed], sel2.idx[listed])
     _check_any_size(sel2, p)
     hsel = _Sel(sel2)
     out_h = out.cpu()
