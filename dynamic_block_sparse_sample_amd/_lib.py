@@ -69,6 +69,7 @@ SIGNATURES = {
     "rra_block_scores": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_top_tau": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P]),
     "rra_estimate": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, ctypes.c_size_t, _P, _P, _P, _P, _P]),
+    "rra_estimate_noalloc": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P]),
     "rra_block_mass": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_xattn_block_scores": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P]),
     "rra_sparse_attn": (ctypes.c_int, [ctypes.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -300,6 +301,25 @@ def estimate(p: Params, q: torch.Tensor, k: torch.Tensor, workspace: torch.Tenso
     _check("rra_estimate",
            lib().rra_estimate(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(workspace), ws_bytes,
                               _ptr(out.mask), _ptr(out.idx), _ptr(out.cnt), _ptr(out.score), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # RRA_NOALLOC_SCRATCH_BYTES
+
+
+def estimate_noalloc(p: Params, q: torch.Tensor, k: torch.Tensor, out: Selection, stream=None) -> Selection:
+    """rra_estimate_noalloc: the estimator with its intermediates in the
+    library's own device array (no workspace).  `out` supplies every output
+    buffer (the binding allocates nothing here either)."""
+    qs, kv, nb, _ = _shapes(p)
+    _need(q, "q", torch.bfloat16, qs)
+    _need(k, "k", torch.bfloat16, kv)
+    _selection_buffers(p, q.device, out.mask, out.idx, out.cnt)
+    if out.score is not None:
+        _need(out.score, "score", torch.float32, (p.batch, p.num_heads, nb, nb))
+    _check("rra_estimate_noalloc",
+           lib().rra_estimate_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out.mask), _ptr(out.idx),
+                                      _ptr(out.cnt), _ptr(out.score), _stream(stream)))
     return out
 
 

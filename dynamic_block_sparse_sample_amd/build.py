@@ -31,6 +31,7 @@ SOURCES = [
     "kernels/block_mass.hip",
     "kernels/xattn_scores.hip",
     "kernels/flash_attn.hip",
+    "rra_noalloc.hip",
 ]
 
 ARCH = "gfx950"

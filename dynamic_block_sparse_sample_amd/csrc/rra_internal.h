@@ -18,6 +18,9 @@ constexpr int kSchedQueues = 8;
 constexpr int kSchedStride = 32;  // uint32 words between counters
 constexpr size_t kSchedBytes = sizeof(uint32_t) * kSchedQueues * kSchedStride;
 
+// Device array behind rra_estimate_noalloc (one per GPU, held until exit).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
 struct Shape {
   int Bz, H, Hkv, L, d, S, Bk;
   int G;   // H / Hkv

@@ -12,7 +12,9 @@
  *    DEVICE pointers to memory the caller allocated and owns.  The library
  *    never allocates or frees device memory, never synchronises, and keeps no
  *    mutable global state, so calls on different streams may run concurrently
- *    as long as their output buffers do not overlap.
+ *    as long as their output buffers do not overlap.  The one exception is
+ *    rra_estimate_noalloc, whose intermediates live in a device array of the
+ *    library (see there).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the null
  *    stream).  A successful return means the kernels were enqueued.
  *  - Layouts are dense row-major:
@@ -150,6 +152,25 @@ rra_status_t rra_top_tau(const rra_params_t* p, const float* score, uint8_t* mas
 rra_status_t rra_estimate(const rra_params_t* p, const void* q, const void* k, void* workspace,
                           size_t workspace_bytes, uint8_t* mask, int32_t* idx, int32_t* cnt,
                           float* score, void* stream);
+
+/* Size of the device array behind rra_estimate_noalloc, per GPU. */
+#define RRA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* rra_estimate for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as rra_estimate, with no workspace argument.
+ * Its intermediates (the aggregated keys, and the block scores when `score`
+ * is NULL) go to a file-scope device array of RRA_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds from its first use until the process
+ * ends.  Needs Bz*Hkv*ceil(L/S)*d*2 bytes with `score` given, that rounded up
+ * to 256 plus Bz*H*Nb*Nb*4 with `score` NULL; a larger problem returns
+ * RRA_ERR_WORKSPACE and enqueues nothing.  Calls on one GPU share its array
+ * (the last call's contents stay there; nothing in it needs clearing), so
+ * calls that overlap in time on the same GPU race: serialise them.  Other
+ * arguments, checks and outputs as rra_estimate.  No allocating call is made
+ * (the array's device address is looked up once per device). */
+rra_status_t rra_estimate_noalloc(const rra_params_t* p, const void* q, const void* k, uint8_t* mask,
+                                  int32_t* idx, int32_t* cnt, float* score, void* stream);
 
 /* XAttention's antidiagonal block scores, the comparison estimator for
  * pattern-search time (RR §2.2, §4.2; XAttention summary): inside each S x S
