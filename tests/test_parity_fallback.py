@@ -1,4 +1,4 @@
-"""The attention kernel's exact-max rerun (needs gfx950).
+"""Rows with logits far above their first key sub-tile's (needs gfx950).
 
 The fast pass fixes each row's reference max from its first key sub-tile; a
 row whose later logits lie far above it (probabilities past 2^64, or past the
@@ -85,3 +85,36 @@ def test_rows_past_the_fast_range_are_exact(d, Bk):
         assert err <= OUT_ATOL
         # the planted rows attend (almost) only to their aligned key
         assert np.max(np.abs(ref[0, 0, 420] - vn[0, 0, 290])) < 1e-6
+
+
+@pytest.mark.parametrize("d,S,Bk", [(128, 16, 128), (64, 8, 64)])
+def test_block_scores_rows_past_the_fast_range(d, S, Bk):
+    """Stride scores far above the rest of a row (~1000 in base-2 units) reach
+    the estimator's softmax: head 0 samples offset 0, so its query at token
+    100 S is aligned with the keys of stride 50 (all equal, so their mean is
+    exact).  Block scores within 1e-5 of the oracle and masks under the
+    near-tie rule."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from helpers import SCORE_ATOL, compare_masks  # noqa: E402
+    H, Hkv, L = 4, 2, 2048
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, H, L, d, generator=g)
+    k = torch.randn(1, Hkv, L, d, generator=g)
+    q[0, 0, 100 * S] = 8.0
+    k[0, 0, 50 * S:51 * S] = 8.0
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    p = rra.make_params(1, H, Hkv, L, d, S, Bk, 0.9)
+    prm = orc.Params(1, H, Hkv, L, d, S, Bk, float(np.float32(0.9)), True)
+    sel = rra.estimate(p, q.cuda(), k.cuda(), return_score=True)
+    torch.cuda.synchronize()
+    m_or = orc.block_scores(to_f64(q), to_f64(k), prm)
+    got = to_f64(sel.score)
+    assert np.all(np.isfinite(got))
+    err = float(np.max(np.abs(got - m_or)))
+    row = (100 * S) // Bk
+    print(f"d={d} S={S}: score err {err:.2e}, planted row mass on block {(50 * S) // Bk}: "
+          f"{got[0, 0, row, (50 * S) // Bk]:.4f}", flush=True)
+    assert err <= SCORE_ATOL
+    checked, near, bad = compare_masks(sel.mask.cpu().numpy(), sel.cnt.cpu().numpy(), sel.idx.cpu().numpy(),
+                                       m_or, prm)
+    assert not bad, bad[:3]
