@@ -19,11 +19,13 @@
 // sampled queries it holds (a zero row when it holds none).  Without
 // causality every stride and key block is visible.
 //
-// Two passes over the visible strides j <= i: pass 1 finds the row max and
-// the softmax denominator (online, base-2), pass 2 recomputes the scores,
-// normalises them and sums them into block cells
+// Two passes over the visible strides j <= i: pass 1 finds a reference max
+// per row (its first tile's max) and the softmax denominator against it
+// (base 2; the exact running max only if a denominator leaves [0, 2^100]),
+// pass 2 recomputes the scores, normalises them and sums them into block cells
 //   score[b,h,I,J] = (1/r) sum_{i in I} sum_{j in J, j <= i} p[i,j]
-// with in-lane adds plus DPP / permlane sums over the r queries of a head.
+// with in-lane adds, one permlane32 exchange per two blocks (each lane half
+// then finishes a different block) and DPP sums over the r queries of a head.
 // Kagg tiles (32 aggregated keys) are staged once per workgroup in LDS, rows
 // padded by 16 bytes so the A-operand reads of 32 rows are free of bank
 // conflicts, double-buffered with the next tile's loads in registers: the
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   constexpr int CPT = 32 * RC / (kBsWaves * 64);  // chunks each thread stages per tile
   static_assert(32 * RC % (kBsWaves * 64) == 0, "staging split");
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][32 * PITCH];
+  __shared__ int s_redo;
 
   const int tid = threadIdx.x;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,12 +119,25 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   jlim = __builtin_amdgcn_readfirstlane(jlim);
 
   // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1).
-  auto load_regs = [&](int jt, u32x4 (&r)[CPT]) {
+  // Whole tiles: a uniform base plus a fixed lane offset per chunk.
+  int lane_off[CPT];
 #pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int ch = tid + e * kBsWaves * 64;
-      const int64_t jrow = min(jt * 32 + ch / RC, Ns - 1);
-      r[e] = *reinterpret_cast<const u32x4*>(kbase + jrow * D + (ch % RC) * 8);
+  for (int e = 0; e < CPT; ++e) {
+    const int ch = tid + e * kBsWaves * 64;
+    lane_off[e] = ((ch / RC) * D + (ch % RC) * 8) * 2;  // bytes
+  }
+  auto load_regs = [&](int jt, u32x4 (&r)[CPT]) {
+    if (jt * 32 + 31 < Ns) {
+      const uint8_t* tb = reinterpret_cast<const uint8_t*>(kbase) + static_cast<int64_t>(jt) * 32 * D * 2;
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) r[e] = *reinterpret_cast<const u32x4*>(tb + lane_off[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        const int ch = tid + e * kBsWaves * 64;
+        const int64_t jrow = min(jt * 32 + ch / RC, Ns - 1);
+        r[e] = *reinterpret_cast<const u32x4*>(kbase + jrow * D + (ch % RC) * 8);
+      }
     }
   };
   auto store_lds = [&](int buf, const u32x4 (&r)[CPT]) {
@@ -182,8 +198,41 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   };
 
   // ---- pass 1: row max and denominator (base-2 logits) ----
+  // Each row's reference max is the max over its first tile, which holds
+  // stride 0 (always visible), and serves the whole row, so the later tiles
+  // need no max and the denominator is never rescaled.  Later scores may lie
+  // above it; if some row's denominator ends outside [0, 2^100] (a score far
+  // above the first tile's), the workgroup runs pass 1 again with the exact
+  // running max.  Either way pass 2 normalises with the (m, z) pass 1 left.
   float m = -INFINITY, z = 0.0f;
-  auto pass1 = [&](int jt, const floatx16& acc) {
+  auto pass1_ref = [&](int jt, const floatx16& acc) {
+    if (jt * 32 + 31 <= jlim) {
+      if (jt == 0) {
+        float tm = acc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) tm = fmaxf(tm, acc[v]);
+        m = tm * c;
+      }
+      float zz = z;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) zz += fast_exp2(fmaf(acc[v], c, -m));
+      z = zz;
+    } else {
+      float x[16];
+      masked(jt, acc, x);
+      if (jt == 0) {
+        float tm = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tm = fmaxf(tm, x[v]);
+        m = (tm > -INFINITY) ? tm : 0.0f;  // a lane without a sampled query: any finite value
+      }
+      float zz = z;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) zz += (x[v] > -INFINITY) ? fast_exp2(x[v] - m) : 0.0f;
+      z = zz;
+    }
+  };
+  auto pass1_exact = [&](int jt, const floatx16& acc) {
     if (jt * 32 + 31 <= jlim) {
       float tm = acc[0];
 #pragma unroll
@@ -210,7 +259,15 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
       }
     }
   };
-  over_tiles(pass1);
+  if (tid == 0) s_redo = 0;  // read only after the barriers of pass 1
+  over_tiles(pass1_ref);
+  if (has_q && !(z <= 0x1p100f)) s_redo = 1;
+  __syncthreads();
+  if (s_redo) {
+    m = -INFINITY;
+    z = 0.0f;
+    over_tiles(pass1_exact);
+  }
   {
     const float mo = shfl_xor_f(m, 32);
     const float zo = shfl_xor_f(z, 32);
@@ -244,16 +301,31 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
       constexpr int NJ = 32 / R;
       float part[NJ];
 #pragma unroll
-      for (int u = 0; u < NJ; ++u) part[u] = 0.0f;
+      for (int u = 0; u < NJ; ++u) part[u] = e[(u * R) / 2];  // first value of block u in this lane
 #pragma unroll
-      for (int v = 0; v < 16; ++v) part[(8 * (v >> 2)) / R] += e[v];
+      for (int v = 0; v < 16; ++v)
+        if (v != ((8 * (v >> 2)) / R) * R / 2) part[(8 * (v >> 2)) / R] += e[v];
+      if constexpr (NJ >= 2) {
+        // Blocks u and u+1 in one exchange: afterwards lanes 0-31 hold block
+        // u's sum over both halves, lanes 32-63 block u+1's.
 #pragma unroll
-      for (int u = 0; u < NJ; ++u) part[u] = group_sum<R>(sum_halves(part[u] * invz));
-      if (valid && half == 0 && (col % R) == 0) {
+        for (int u = 0; u < NJ; u += 2) {
+          const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[u]), __float_as_uint(part[u + 1]),
+                                                          false, false);
+          part[u / 2] = group_sum<R>((__uint_as_float(w[0]) + __uint_as_float(w[1])) * invz);
+        }
+        if (valid && (col % R) == 0) {
 #pragma unroll
-        for (int u = 0; u < NJ; ++u) {
-          const int J = jt * NJ + u;
-          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+          for (int u = 0; u < NJ; u += 2) {
+            const int J = jt * NJ + u + half;
+            if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u / 2] * inv_r;
+          }
+        }
+      } else {
+        part[0] = group_sum<R>(sum_halves(part[0]) * invz);
+        if (valid && half == 0 && (col % R) == 0) {
+          const int J = jt;
+          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[0] * inv_r;
         }
       }
     } else {

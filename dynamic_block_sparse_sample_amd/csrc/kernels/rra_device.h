@@ -71,9 +71,11 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppRowMirror = 0x140;  // lane i <- lane 15 - i
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7 - i (in each half row)
 
+// (Every control here stays inside a 16-lane row, so bound_ctrl never applies;
+// setting it lets the compiler fuse the move into the consuming add.)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // Sum of v over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32),
