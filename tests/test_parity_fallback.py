@@ -89,19 +89,30 @@ def test_rows_past_the_fast_range_are_exact(d, Bk):
 
 @pytest.mark.parametrize("d,S,Bk", [(128, 16, 128), (64, 8, 64)])
 def test_block_scores_rows_past_the_fast_range(d, S, Bk):
-    """Stride scores far above the rest of a row (~1000 in base-2 units) reach
-    the estimator's softmax: head 0 samples offset 0, so its query at token
-    100 S is aligned with the keys of stride 50 (all equal, so their mean is
-    exact).  Block scores within 1e-5 of the oracle and masks under the
-    near-tie rule."""
+    """Stride scores far above the first tile of their row reach the
+    estimator's softmax.  Head 0 samples offset 0.  Its query at token 100 S
+    (channels [0, d/2) = 8) is aligned with the keys of stride 50 (the same
+    channels = 8): a base-2 logit about 520 above the rest (370 at d = 64),
+    past the float32 range, so the denominator overflows and pass 1 runs
+    again with the exact max.  Its query at token 120 S (channels [d/2, d) = 8)
+    is aligned with the keys of stride 70 (the same channels = 0.92): about 60
+    above the rest (42 at d = 64), which keeps the denominator finite but puts
+    probabilities far above 1 against the first tile's reference.  Every key of a planted stride
+    is equal, so its mean is exact.  Block scores within 1e-5 of the oracle
+    and masks under the near-tie rule."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from helpers import SCORE_ATOL, compare_masks  # noqa: E402
     H, Hkv, L = 4, 2, 2048
     g = torch.Generator().manual_seed(11)
     q = torch.randn(1, H, L, d, generator=g)
     k = torch.randn(1, Hkv, L, d, generator=g)
-    q[0, 0, 100 * S] = 8.0
-    k[0, 0, 50 * S:51 * S] = 8.0
+    h2 = d // 2
+    q[0, 0, 100 * S, :h2] = 8.0
+    q[0, 0, 100 * S, h2:] = 0.0
+    k[0, 0, 50 * S:51 * S, :h2] = 8.0
+    q[0, 0, 120 * S, :h2] = 0.0
+    q[0, 0, 120 * S, h2:] = 8.0
+    k[0, 0, 70 * S:71 * S, h2:] = 0.92
     q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
     p = rra.make_params(1, H, Hkv, L, d, S, Bk, 0.9)
     prm = orc.Params(1, H, Hkv, L, d, S, Bk, float(np.float32(0.9)), True)
@@ -111,9 +122,12 @@ def test_block_scores_rows_past_the_fast_range(d, S, Bk):
     got = to_f64(sel.score)
     assert np.all(np.isfinite(got))
     err = float(np.max(np.abs(got - m_or)))
-    row = (100 * S) // Bk
-    print(f"d={d} S={S}: score err {err:.2e}, planted row mass on block {(50 * S) // Bk}: "
-          f"{got[0, 0, row, (50 * S) // Bk]:.4f}", flush=True)
+    for tok, stride in ((100 * S, 50), (120 * S, 70)):
+        row, col = tok // Bk, (stride * S) // Bk
+        print(f"d={d} S={S}: planted row {row} mass on block {col}: GPU {got[0, 0, row, col]:.4f}, "
+              f"oracle {m_or[0, 0, row, col]:.4f}", flush=True)
+        assert m_or[0, 0, row, col] > 0.1  # the planted stride dominates its query's softmax
+    print(f"d={d} S={S}: score err {err:.2e}", flush=True)
     assert err <= SCORE_ATOL
     checked, near, bad = compare_masks(sel.mask.cpu().numpy(), sel.cnt.cpu().numpy(), sel.idx.cpu().numpy(),
                                        m_or, prm)
