@@ -67,6 +67,81 @@ class Timer:
         return [a.elapsed_time(b) for a, b in ev]
 
 
+class ClockSampler:
+    """GFX clock in MHz (mean over the XCDs) read with `amd-smi metric --clock`
+    from a thread while GPU work runs; summary() keeps the samples taken inside
+    a time window.  Without amd-smi it records nothing."""
+
+    def __init__(self, period_s: float = 0.1):
+        import shutil
+        import threading
+
+        self.samples = []
+        self.period_s = period_s
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if shutil.which("amd-smi") else None
+
+    def _read(self):
+        import subprocess
+
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True, timeout=10)
+        d = json.loads(r.stdout)
+        gpus = d["gpu_data"] if isinstance(d, dict) else d
+        vals = []
+        for name, entry in gpus[0]["clock"].items():
+            clk = entry.get("clk") if isinstance(entry, dict) else None
+            v = clk.get("value") if isinstance(clk, dict) else None  # "N/A" entries are strings
+            if name.startswith("gfx_") and isinstance(v, (int, float)):
+                vals.append(float(v))
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            t = time.time()
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append((t, time.time(), v))
+            except Exception:
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self._thread is not None:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=15)
+
+    def summary(self, t0: float, t1: float):
+        """Readings whose call began and ended inside [t0, t1]."""
+        vals = sorted(v for ta, tb, v in self.samples if t0 <= ta and tb <= t1)
+        if not vals:
+            return None
+        return {"samples": len(vals), "median": round(vals[len(vals) // 2], 1), "min": round(vals[0], 1),
+                "max": round(vals[-1], 1)}
+
+
+def clock_during(fn, secs: float):
+    """GFX clock readings while fn (which synchronises) runs back to back for
+    about secs seconds."""
+    with ClockSampler() as cs:
+        time.sleep(0.2)
+        t0 = time.time()
+        n = 0
+        while time.time() - t0 < secs:
+            fn()
+            n += 1
+        t1 = time.time()
+    out = cs.summary(t0, t1)
+    if out is not None:
+        out["runs"] = n
+    return out
+
+
 def stats(ms):
     v = sorted(ms)
     return {"median": round(v[len(v) // 2], 4), "min": round(v[0], 4), "mean": round(sum(v) / len(v), 4),
@@ -458,6 +533,11 @@ def main(argv=None) -> int:
         "estimator_kernels_ms": brk,
         **estimator_fracs(p, sum_cnt, t_est, brk["stride_aggregate"]["median"]),
         "dense_attn_tflops": round(f_dense / (t_dense * 1e-3) / 1e12, 2),
+        # GFX clock (amd-smi, mean over the XCDs), read after the timed region while the step and the
+        # dense launch each run back to back for a few seconds
+        "gpu_clock_mhz": {"step": clock_during(lambda: (step(), torch.cuda.synchronize()), 4.0),
+                          "dense_attn": clock_during(lambda: (rra.dense_attn(p, qd, kd, vd, out=dense_out),
+                                                              torch.cuda.synchronize()), 4.0)},
         "roofline": {"kernel": "flash_attn_kernel<128,128> (rra_sparse_attn)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
