@@ -28,9 +28,10 @@
 // then finishes a different block) and DPP sums over the r queries of a head.
 // Kagg tiles (32 aggregated keys) are staged once per workgroup in LDS, rows
 // padded by 16 bytes so the A-operand reads of 32 rows are free of bank
-// conflicts, double-buffered with the next tile's loads in registers: the
-// four waves share every tile, a quarter of the L2 traffic of one wave per
-// query block (which bound this kernel).
+// conflicts, in chunks of two tiles double-buffered with the next chunk's
+// loads in registers (one barrier per chunk): the four waves share every
+// tile, a quarter of the L2 traffic of one wave per query block (which bound
+// this kernel).
 #include <climits>
 #include <cmath>
 
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   constexpr int RC = D / 8;              // 16-byte chunks per row
   constexpr int CPT = 32 * RC / (kBsWaves * 64);  // chunks each thread stages per tile
   static_assert(32 * RC % (kBsWaves * 64) == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) uint8_t kt[2][32 * PITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t kt[4][32 * PITCH];
   __shared__ int s_redo;
 
   const int tid = threadIdx.x;
@@ -153,40 +154,56 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   };
   // Runs f(jt, S^T tile) over the wave's tiles, software-pipelined: the MFMAs
   // of tile jt+1 are issued before f works on tile jt, so the MFMA unit and
-  // the VALU overlap inside the wave.  Every wave takes part in the staging
-  // and the barriers of all ntile_wg tiles.  Tiles jt and jt+1 sit in the two
-  // LDS buffers during step jt; tile jt+2 replaces tile jt at the end of the
-  // step, after the barrier that followed every wave's reads of tile jt.
+  // the VALU overlap inside the wave.  Tiles are staged in chunks of two
+  // (chunk c = tiles 2c, 2c+1 in LDS set c & 1) with one barrier per chunk,
+  // placed between the chunk's two tiles: iteration c issues the MFMAs of
+  // tile 2c+1, works on tile 2c, stores chunk c+1 into the other set (whose
+  // tiles every wave had read before the previous barrier), waits at the
+  // barrier, then issues the MFMAs of tile 2c+2 and works on tile 2c+1.
+  // Every wave takes part in the staging and the barriers of all ntile_wg tiles.
   auto over_tiles = [&](auto&& f) {
-    u32x4 r[CPT];
-    load_regs(0, r);
-    store_lds(0, r);
-    if (ntile_wg > 1) {
-      load_regs(1, r);
-      store_lds(1, r);
-    }
+    const int nchunk = (ntile_wg + 1) / 2;
+    u32x4 r[2][CPT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < ntile_wg) {
+        load_regs(i, r[i]);
+        store_lds(i, r[i]);
+      }
     __syncthreads();
-    floatx16 acc_cur, acc_next;
+    floatx16 acc_a, acc_b;
     if (ntile > 0) {
       u32x4 a[KC];
       frag(0, a);
-      acc_cur = tile_mma<D>(a, qb);
+      acc_a = tile_mma<D>(a, qb);
     }
-    __syncthreads();  // every wave has read tile 0 before step 0 refills its buffer
-    for (int jt = 0; jt < ntile_wg; ++jt) {
-      const int buf = jt & 1;
-      const bool refill = jt + 2 < ntile_wg;
-      if (refill) load_regs(jt + 2, r);
-      if (jt + 1 < ntile) {
-        u32x4 a[KC];
-        frag(buf ^ 1, a);
-        acc_next = tile_mma<D>(a, qb);
+    for (int c = 0; c < nchunk; ++c) {
+      const int set = c & 1;
+      const int t0 = 2 * c, t1 = 2 * c + 1, t2 = 2 * c + 2;
+      const bool refill = t2 < ntile_wg;
+      if (refill) {
+        load_regs(t2, r[0]);
+        if (t2 + 1 < ntile_wg) load_regs(t2 + 1, r[1]);
       }
-      if (jt < ntile) f(jt, acc_cur);
-      if (refill) store_lds(buf, r);
+      if (t1 < ntile) {
+        u32x4 a[KC];
+        frag(2 * set + 1, a);
+        acc_b = tile_mma<D>(a, qb);
+      }
+      if (t0 < ntile) f(t0, acc_a);
+      if (refill) {
+        store_lds(2 * (set ^ 1), r[0]);
+        if (t2 + 1 < ntile_wg) store_lds(2 * (set ^ 1) + 1, r[1]);
+      }
       __syncthreads();
-      acc_cur = acc_next;
+      if (t2 < ntile) {
+        u32x4 a[KC];
+        frag(2 * (set ^ 1), a);
+        acc_a = tile_mma<D>(a, qb);
+      }
+      if (t1 < ntile) f(t1, acc_b);
     }
+    __syncthreads();  // every wave is done with both sets before they are restaged
   };
   // Masked base-2 logits of tile jt (only the tiles that reach past jlim).
   auto masked = [&](int jt, const floatx16& acc, float (&x)[16]) {
