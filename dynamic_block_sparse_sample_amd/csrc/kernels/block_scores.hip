@@ -26,16 +26,18 @@
 //   score[b,h,I,J] = (1/r) sum_{i in I} sum_{j in J, j <= i} p[i,j]
 // with in-lane adds, one permlane32 exchange per two blocks (each lane half
 // then finishes a different block) and DPP sums over the r queries of a head.
-// Kagg tiles (32 aggregated keys) are staged once per workgroup in LDS, rows
-// padded by 16 bytes so the A-operand reads of 32 rows are free of bank
-// conflicts, in chunks of two tiles double-buffered with the next chunk's
-// loads in registers (one barrier per chunk): the four waves share every
-// tile, a quarter of the L2 traffic of one wave per query block (which bound
-// this kernel).
+// Kagg tiles (32 aggregated keys) are copied once per workgroup straight from
+// global memory into LDS (global_load_lds_dwordx4), each row's 16-byte chunks
+// XOR-swizzled so the A-operand reads of 32 rows are free of bank conflicts,
+// in chunks of two tiles over four buffers (one barrier per chunk; a chunk's
+// copies have a whole iteration to land): the four waves share every tile, a
+// quarter of the L2 traffic of one wave per query block (which bound this
+// kernel).
 #include <climits>
 #include <cmath>
 
 #include "../rra_internal.h"
+#include "lds_copy.h"
 #include "rra_device.h"
 
 namespace rra {
@@ -60,11 +62,16 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
                                                           int nbg, float c, int rr_step, int rr_shift,
                                                           int causal) {
   constexpr int KC = D / 16;
-  constexpr int PITCH = D * 2 + 16;      // LDS bytes per aggregated-key row
-  constexpr int RC = D / 8;              // 16-byte chunks per row
-  constexpr int CPT = 32 * RC / (kBsWaves * 64);  // chunks each thread stages per tile
-  static_assert(32 * RC % (kBsWaves * 64) == 0, "staging split");
-  __shared__ __attribute__((aligned(16))) uint8_t kt[4][32 * PITCH];
+  constexpr int ROWB = D * 2;                    // bytes per aggregated-key row
+  constexpr int RC = D / 8;                      // 16-byte chunks per row
+  constexpr int TILEB = 32 * ROWB;               // bytes of one 32-row tile
+  constexpr int ROWS_PER_INST = 64 / RC;         // rows per copy instruction (1 KB)
+  constexpr int IPW = TILEB / 1024 / kBsWaves;   // copy instructions per wave and tile
+  static_assert(TILEB % (1024 * kBsWaves) == 0, "copy split");
+  // Four tile buffers (two chunks of two); chunk c of a row's 16-byte chunks
+  // sits at position c ^ swz(row), which keeps the A-operand reads of 32 rows
+  // free of bank conflicts.
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[4][TILEB];
   __shared__ int s_redo;
 
   const int tid = threadIdx.x;
@@ -119,58 +126,48 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   for (int o = 32; o >= 1; o >>= 1) jlim = min(jlim, __shfl_xor(jlim, o, 64));
   jlim = __builtin_amdgcn_readfirstlane(jlim);
 
-  // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1).
-  // Whole tiles: a uniform base plus a fixed lane offset per chunk.
-  int lane_off[CPT];
-#pragma unroll
-  for (int e = 0; e < CPT; ++e) {
-    const int ch = tid + e * kBsWaves * 64;
-    lane_off[e] = ((ch / RC) * D + (ch % RC) * 8) * 2;  // bytes
-  }
-  auto load_regs = [&](int jt, u32x4 (&r)[CPT]) {
-    if (jt * 32 + 31 < Ns) {
-      const uint8_t* tb = reinterpret_cast<const uint8_t*>(kbase) + static_cast<int64_t>(jt) * 32 * D * 2;
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) r[e] = *reinterpret_cast<const u32x4*>(tb + lane_off[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        const int ch = tid + e * kBsWaves * 64;
-        const int64_t jrow = min(jt * 32 + ch / RC, Ns - 1);
-        r[e] = *reinterpret_cast<const u32x4*>(kbase + jrow * D + (ch % RC) * 8);
-      }
-    }
-  };
-  auto store_lds = [&](int buf, const u32x4 (&r)[CPT]) {
-#pragma unroll
-    for (int e = 0; e < CPT; ++e) {
-      const int ch = tid + e * kBsWaves * 64;
-      *reinterpret_cast<u32x4*>(&kt[buf][(ch / RC) * PITCH + (ch % RC) * 16]) = r[e];
-    }
+  // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1),
+  // copied straight from global memory into LDS buffer buf: IPW 1 KB copy
+  // instructions per wave, lane -> (row, chunk slot), the slot holding the
+  // row's chunk slot ^ swz(row).
+  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kbase);
+  auto copy_tile = [&](int jt, int buf) {
+    const uint32_t l0 = lds_addr(kt[buf]) + wv * IPW * 1024;
+    static_for<IPW>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int r = (wv * IPW + i) * ROWS_PER_INST + lane / RC;  // row inside the tile
+      const int chunk = (lane % RC) ^ (swz(r) & (RC - 1));
+      const int grow = min(jt * 32 + r, Ns - 1);
+      copy16_to_lds<i * 1024>(kbytes, grow * ROWB + chunk * 16, l0);
+    });
   };
   auto frag = [&](int buf, u32x4 (&a)[KC]) {
+    const int sw = swz(col) & (RC - 1);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(&kt[buf][col * PITCH + (2 * kc + half) * 16]);
+    for (int kc = 0; kc < KC; ++kc)
+      a[kc] = *reinterpret_cast<const u32x4*>(&kt[buf][col * ROWB + (((2 * kc + half) ^ sw) * 16)]);
   };
   // Runs f(jt, S^T tile) over the wave's tiles, software-pipelined: the MFMAs
   // of tile jt+1 are issued before f works on tile jt, so the MFMA unit and
   // the VALU overlap inside the wave.  Tiles are staged in chunks of two
   // (chunk c = tiles 2c, 2c+1 in LDS set c & 1) with one barrier per chunk,
   // placed between the chunk's two tiles: iteration c issues the MFMAs of
-  // tile 2c+1, works on tile 2c, stores chunk c+1 into the other set (whose
-  // tiles every wave had read before the previous barrier), waits at the
-  // barrier, then issues the MFMAs of tile 2c+2 and works on tile 2c+1.
-  // Every wave takes part in the staging and the barriers of all ntile_wg tiles.
+  // tile 2c+1 and works on tile 2c, waits for its copies of chunk c+1 and at
+  // the barrier (after which every wave is done with chunk c and chunk c+1 is
+  // in LDS), starts the copies of chunk c+2 into chunk c's set, then issues
+  // the MFMAs of tile 2c+2 and works on tile 2c+1.  A chunk's copies so have
+  // a whole iteration to land.  Every wave takes part in the copies and the
+  // barriers of all ntile_wg tiles.
   auto over_tiles = [&](auto&& f) {
     const int nchunk = (ntile_wg + 1) / 2;
-    u32x4 r[2][CPT];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i < ntile_wg) {
-        load_regs(i, r[i]);
-        store_lds(i, r[i]);
-      }
-    __syncthreads();
+    auto copy_chunk = [&](int c, int set) {
+      if (2 * c < ntile_wg) copy_tile(2 * c, 2 * set);
+      if (2 * c + 1 < ntile_wg) copy_tile(2 * c + 1, 2 * set + 1);
+    };
+    copy_chunk(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();  // chunk 0 in LDS
+    if (nchunk > 1) copy_chunk(1, 1);
     floatx16 acc_a, acc_b;
     if (ntile > 0) {
       u32x4 a[KC];
@@ -180,22 +177,15 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
     for (int c = 0; c < nchunk; ++c) {
       const int set = c & 1;
       const int t0 = 2 * c, t1 = 2 * c + 1, t2 = 2 * c + 2;
-      const bool refill = t2 < ntile_wg;
-      if (refill) {
-        load_regs(t2, r[0]);
-        if (t2 + 1 < ntile_wg) load_regs(t2 + 1, r[1]);
-      }
       if (t1 < ntile) {
         u32x4 a[KC];
         frag(2 * set + 1, a);
         acc_b = tile_mma<D>(a, qb);
       }
       if (t0 < ntile) f(t0, acc_a);
-      if (refill) {
-        store_lds(2 * (set ^ 1), r[0]);
-        if (t2 + 1 < ntile_wg) store_lds(2 * (set ^ 1) + 1, r[1]);
-      }
+      wait_vmcnt<0>();
       __syncthreads();
+      if (c + 2 < nchunk) copy_chunk(c + 2, set);
       if (t2 < ntile) {
         u32x4 a[KC];
         frag(2 * (set ^ 1), a);
