@@ -68,9 +68,7 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   constexpr int ROWS_PER_INST = 64 / RC;         // rows per copy instruction (1 KB)
   constexpr int IPW = TILEB / 1024 / kBsWaves;   // copy instructions per wave and tile
   static_assert(TILEB % (1024 * kBsWaves) == 0, "copy split");
-  // Four tile buffers (two chunks of two); chunk c of a row's 16-byte chunks
-  // sits at position c ^ swz(row), which keeps the A-operand reads of 32 rows
-  // free of bank conflicts.
+  // Four tile buffers (two chunks of two).
   __shared__ __attribute__((aligned(1024))) uint8_t kt[4][TILEB];
   __shared__ int s_redo;
 
@@ -126,72 +124,107 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
   for (int o = 32; o >= 1; o >>= 1) jlim = min(jlim, __shfl_xor(jlim, o, 64));
   jlim = __builtin_amdgcn_readfirstlane(jlim);
 
-  // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1),
-  // copied straight from global memory into LDS buffer buf: IPW 1 KB copy
-  // instructions per wave, lane -> (row, chunk slot), the slot holding the
-  // row's chunk slot ^ swz(row).
-  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kbase);
-  auto copy_tile = [&](int jt, int buf) {
-    const uint32_t l0 = lds_addr(kt[buf]) + wv * IPW * 1024;
-    static_for<IPW>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      const int r = (wv * IPW + i) * ROWS_PER_INST + lane / RC;  // row inside the tile
-      const int chunk = (lane % RC) ^ (swz(r) & (RC - 1));
-      const int grow = min(jt * 32 + r, Ns - 1);
-      copy16_to_lds<i * 1024>(kbytes, grow * ROWB + chunk * 16, l0);
-    });
-  };
-  auto frag = [&](int buf, u32x4 (&a)[KC]) {
+  // Per-lane byte offsets that stay fixed for the whole kernel, kept in
+  // registers (the empty asm makes them opaque, so the compiler does not
+  // recompute them for every tile): fa[kc], the A-operand chunk of row col
+  // inside a tile buffer (the buffer itself is an immediate offset), and
+  // vo[i], the source of copy instruction i relative to the tile's first row.
+  // A tile buffer holds row r's chunk slot s at position s ^ swz(r), which
+  // keeps the A-operand reads of 32 rows free of bank conflicts.
+  uint32_t fa[KC];
+  {
     const int sw = swz(col) & (RC - 1);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      a[kc] = *reinterpret_cast<const u32x4*>(&kt[buf][col * ROWB + (((2 * kc + half) ^ sw) * 16)]);
+    for (int kc = 0; kc < KC; ++kc) {
+      fa[kc] = col * ROWB + (((2 * kc + half) ^ sw) * 16);
+      asm volatile("" : "+v"(fa[kc]));
+    }
+  }
+  int vr[IPW], vo[IPW];  // row inside the tile, source offset
+  static_for<IPW>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    vr[i] = (wv * IPW + i) * ROWS_PER_INST + lane / RC;
+    vo[i] = vr[i] * ROWB + (((lane % RC) ^ (swz(vr[i]) & (RC - 1))) * 16);
+    asm volatile("" : "+v"(vo[i]));
+  });
+
+  // Tile jt = aggregated keys jt*32 .. jt*32+31 (rows past Ns repeat row Ns-1),
+  // copied straight from global memory into LDS buffer BUF: IPW 1 KB copy
+  // instructions per wave, lane -> (row, chunk slot).
+  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(kbase);
+  auto copy_tile = [&](int jt, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint32_t l0 = lds_addr(kt[BUF]) + wv * IPW * 1024;
+    const uint8_t* gt = kbytes + static_cast<int64_t>(jt) * 32 * ROWB;
+    if (jt * 32 + 32 <= Ns) {
+      static_for<IPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        copy16_to_lds<i * 1024>(gt, vo[i], l0);
+      });
+    } else {
+      static_for<IPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int over = max(0, jt * 32 + vr[i] - (Ns - 1));
+        copy16_to_lds<i * 1024>(gt, vo[i] - over * ROWB, l0);
+      });
+    }
+  };
+  auto frag = [&](auto bufc, u32x4 (&a)[KC]) {
+    constexpr int BUF = decltype(bufc)::value;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a[kc] = *reinterpret_cast<const u32x4*>(&kt[BUF][fa[kc]]);
   };
   // Runs f(jt, S^T tile) over the wave's tiles, software-pipelined: the MFMAs
   // of tile jt+1 are issued before f works on tile jt, so the MFMA unit and
   // the VALU overlap inside the wave.  Tiles are staged in chunks of two
-  // (chunk c = tiles 2c, 2c+1 in LDS set c & 1) with one barrier per chunk,
-  // placed between the chunk's two tiles: iteration c issues the MFMAs of
-  // tile 2c+1 and works on tile 2c, waits for its copies of chunk c+1 and at
-  // the barrier (after which every wave is done with chunk c and chunk c+1 is
-  // in LDS), starts the copies of chunk c+2 into chunk c's set, then issues
-  // the MFMAs of tile 2c+2 and works on tile 2c+1.  A chunk's copies so have
-  // a whole iteration to land.  Every wave takes part in the copies and the
-  // barriers of all ntile_wg tiles.
+  // (chunk c = tiles 2c, 2c+1 in LDS set c & 1, buffers 2(c & 1) and
+  // 2(c & 1) + 1) with one barrier per chunk, placed between the chunk's two
+  // tiles: step c issues the MFMAs of tile 2c+1 and works on tile 2c, waits
+  // for its copies of chunk c+1 and at the barrier (after which every wave is
+  // done with chunk c and chunk c+1 is in LDS), starts the copies of chunk
+  // c+2 into chunk c's set, then issues the MFMAs of tile 2c+2 and works on
+  // tile 2c+1.  A chunk's copies so have a whole step to land.  Steps come in
+  // pairs (sets 0 and 1), so every buffer index is a constant.  Every wave
+  // takes part in the copies and the barriers of all ntile_wg tiles.
   auto over_tiles = [&](auto&& f) {
     const int nchunk = (ntile_wg + 1) / 2;
-    auto copy_chunk = [&](int c, int set) {
-      if (2 * c < ntile_wg) copy_tile(2 * c, 2 * set);
-      if (2 * c + 1 < ntile_wg) copy_tile(2 * c + 1, 2 * set + 1);
+    auto copy_chunk = [&](int c, auto setc) {
+      constexpr int SET = decltype(setc)::value;
+      if (2 * c < ntile_wg) copy_tile(2 * c, std::integral_constant<int, 2 * SET>{});
+      if (2 * c + 1 < ntile_wg) copy_tile(2 * c + 1, std::integral_constant<int, 2 * SET + 1>{});
     };
-    copy_chunk(0, 0);
+    copy_chunk(0, std::integral_constant<int, 0>{});
     wait_vmcnt<0>();
     __syncthreads();  // chunk 0 in LDS
-    if (nchunk > 1) copy_chunk(1, 1);
+    if (nchunk > 1) copy_chunk(1, std::integral_constant<int, 1>{});
     floatx16 acc_a, acc_b;
     if (ntile > 0) {
       u32x4 a[KC];
-      frag(0, a);
+      frag(std::integral_constant<int, 0>{}, a);
       acc_a = tile_mma<D>(a, qb);
     }
-    for (int c = 0; c < nchunk; ++c) {
-      const int set = c & 1;
+    auto step = [&](int c, auto setc) {
+      constexpr int SET = decltype(setc)::value;
       const int t0 = 2 * c, t1 = 2 * c + 1, t2 = 2 * c + 2;
       if (t1 < ntile) {
         u32x4 a[KC];
-        frag(2 * set + 1, a);
+        frag(std::integral_constant<int, 2 * SET + 1>{}, a);
         acc_b = tile_mma<D>(a, qb);
       }
       if (t0 < ntile) f(t0, acc_a);
       wait_vmcnt<0>();
       __syncthreads();
-      if (c + 2 < nchunk) copy_chunk(c + 2, set);
+      if (c + 2 < nchunk) copy_chunk(c + 2, setc);
       if (t2 < ntile) {
         u32x4 a[KC];
-        frag(2 * (set ^ 1), a);
+        frag(std::integral_constant<int, 2 * (SET ^ 1)>{}, a);
         acc_a = tile_mma<D>(a, qb);
       }
       if (t1 < ntile) f(t1, acc_b);
+    };
+    for (int c = 0; c < nchunk; c += 2) {
+      step(c, std::integral_constant<int, 0>{});
+      if (c + 1 < nchunk) step(c + 1, std::integral_constant<int, 1>{});
     }
     __syncthreads();  // every wave is done with both sets before they are restaged
   };
