@@ -829,13 +829,14 @@ def selection_report(first_workload: str):
 
 
 def _kernel_hash() -> str:
-    """Hash of the attention kernel source (flash_attn.hip and its work-order
-    header fa_order.h); traffic counters are only valid for it."""
+    """Hash of the attention kernel source (flash_attn.hip and the headers of
+    its directory that it includes: the work order, the LDS copies and the
+    device helpers); traffic counters are only valid for it."""
     import hashlib
     kdir = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dynamic_block_sparse_sample_amd", "csrc",
                         "kernels")
     h = hashlib.sha256()
-    for name in ("flash_attn.hip", "fa_order.h"):
+    for name in ("flash_attn.hip", "fa_order.h", "lds_copy.h", "rra_device.h"):
         with open(os.path.join(kdir, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
