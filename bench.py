@@ -663,20 +663,21 @@ def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
     th = threading.Thread(target=sampler, daemon=True)
     th.start()
     phases = []
-    time.sleep(2.0)
-    phases.append(("idle", time.time() - 2.0, time.time(), None))
-    for name, fn, flops in (("sparse_attn", sparse_fn, f_sparse), ("dense_attn", dense_fn, f_dense)):
-        fn()
-        torch.cuda.synchronize()
-        t0, n = time.time(), 0
-        while time.time() - t0 < secs:
+    with ClockSampler(period_s=0.2) as clocks:
+        time.sleep(2.0)
+        phases.append(("idle", time.time() - 2.0, time.time(), None))
+        for name, fn, flops in (("sparse_attn", sparse_fn, f_sparse), ("dense_attn", dense_fn, f_dense)):
             fn()
             torch.cuda.synchronize()
-            n += 1
-        t1 = time.time()
-        phases.append((name, t0, t1, flops * n / (t1 - t0) / 1e12))
-        log(f"[bench] power phase {name}: {n} runs")
-        time.sleep(1.5)
+            t0, n = time.time(), 0
+            while time.time() - t0 < secs:
+                fn()
+                torch.cuda.synchronize()
+                n += 1
+            t1 = time.time()
+            phases.append((name, t0, t1, flops * n / (t1 - t0) / 1e12))
+            log(f"[bench] power phase {name}: {n} runs")
+            time.sleep(1.5)
     stop.set()
     th.join(timeout=15)
     res = {"mode": "power", "samples": len(samples), "phases": {}}
@@ -686,7 +687,7 @@ def power_report(sparse_fn, f_sparse, dense_fn, f_dense, secs) -> dict:
         med = vals[len(vals) // 2] if vals else None
         if name == "idle":
             idle_w = med
-        entry = {"median_w": med, "n_samples": len(vals)}
+        entry = {"median_w": med, "n_samples": len(vals), "gfx_clock_mhz": clocks.summary(t0 + 0.8, t1 - 0.2)}
         if rate is not None:
             entry["tflops"] = round(rate, 1)
             if med is not None and idle_w is not None:
