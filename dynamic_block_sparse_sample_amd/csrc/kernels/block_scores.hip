@@ -22,7 +22,8 @@
 // Two passes over the visible strides j <= i: pass 1 finds a reference max
 // per row (its first tile's max) and the softmax denominator against it
 // (base 2; the exact running max only if a denominator leaves [0, 2^100]),
-// pass 2 recomputes the scores, normalises them and sums them into block cells
+// pass 2 recomputes the scores, normalises them (1/z and 1/r enter the
+// exponent as log2(z r)) and sums them into block cells
 //   score[b,h,I,J] = (1/r) sum_{i in I} sum_{j in J, j <= i} p[i,j]
 // with in-lane adds, one permlane32 exchange per two blocks (each lane half
 // then finishes a different block) and DPP sums over the r queries of a head.
@@ -318,23 +319,26 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
     m = mm;
     z = zt;
   }
-  const float invz = has_q ? 1.0f / z : 0.0f;
-  const float inv_r = (r_I > 0) ? 1.0f / static_cast<float>(r_I) : 0.0f;  // no sampled query: zero row
+  // Pass 2 takes exp2(x - mz) with mz = m + log2(z r_I), which is already the
+  // probability divided by the r_I sampled queries of the block; lanes
+  // without a sampled query use mz = +inf, so theirs are 0.  (A block without
+  // any sampled query so gets a zero row.)
+  const float mz = has_q ? m + __builtin_amdgcn_logf(z * static_cast<float>(r_I)) : INFINITY;
   float* srow_base = score + (static_cast<int64_t>(b) * H * Nb + I) * Nb;  // + h * Nb * Nb + J
 
   const int jlast = causal ? I : Nb - 1;  // last key block of the row
 
   // ---- pass 2: probabilities pooled into block cells ----
   auto pass2 = [&](int jt, const floatx16& acc) {
-    float e[16];  // unnormalised probabilities; 1/z is applied to the in-lane sums
+    float e[16];  // probabilities / r_I
     if (jt * 32 + 31 <= jlim) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -m));
+      for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -mz));
     } else {
       float x[16];
       masked(jt, acc, x);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) e[v] = (x[v] > -INFINITY) ? fast_exp2(x[v] - m) : 0.0f;
+      for (int v = 0; v < 16; ++v) e[v] = (x[v] > -INFINITY) ? fast_exp2(x[v] - mz) : 0.0f;
     }
     if constexpr (R >= 8) {
       // A block spans R >= 8 strides: groups of 4 values (v >> 2) in both lane halves.
@@ -352,20 +356,20 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
         for (int u = 0; u < NJ; u += 2) {
           const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[u]), __float_as_uint(part[u + 1]),
                                                           false, false);
-          part[u / 2] = group_sum<R>((__uint_as_float(w[0]) + __uint_as_float(w[1])) * invz);
+          part[u / 2] = group_sum<R>(__uint_as_float(w[0]) + __uint_as_float(w[1]));
         }
         if (valid && (col % R) == 0) {
 #pragma unroll
           for (int u = 0; u < NJ; u += 2) {
             const int J = jt * NJ + u + half;
-            if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u / 2] * inv_r;
+            if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u / 2];
           }
         }
       } else {
-        part[0] = group_sum<R>(sum_halves(part[0]) * invz);
+        part[0] = group_sum<R>(sum_halves(part[0]));
         if (valid && half == 0 && (col % R) == 0) {
           const int J = jt;
-          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[0] * inv_r;
+          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[0];
         }
       }
     } else {
@@ -378,13 +382,13 @@ __global__ __launch_bounds__(kBsWaves * 64) void block_scores_kernel(const uint1
 #pragma unroll
       for (int v = 0; v < 16; ++v) part[(v >> 2) * PER + (v & 3) / R] += e[v];
 #pragma unroll
-      for (int u = 0; u < NJL; ++u) part[u] = group_sum<R>(part[u] * invz);
+      for (int u = 0; u < NJL; ++u) part[u] = group_sum<R>(part[u]);
       if (valid && (col % R) == 0) {
 #pragma unroll
         for (int u = 0; u < NJL; ++u) {
           const int so = 8 * (u / PER) + 4 * half + R * (u % PER);  // first stride of the block in the tile
           const int J = jt * (32 / R) + so / R;
-          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u] * inv_r;
+          if (J <= jlast) srow_base[static_cast<int64_t>(h) * Nb * Nb + J] = part[u];
         }
       }
     }
