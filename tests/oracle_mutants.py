@@ -51,8 +51,12 @@ def main() -> int:
     bad = 0
     with tempfile.TemporaryDirectory() as tmp:
         dst = os.path.join(tmp, "repo")
-        shutil.copytree(SRC, dst, ignore=shutil.ignore_patterns("_work", "gpurun_out", ".git", "_build", "*.so",
-                                                                 "__pycache__"))
+        os.makedirs(dst)
+        skip = shutil.ignore_patterns("*.so", "*.o", "__pycache__")
+        for name in ("oracle", "tests", "dynamic_block_sparse_sample_amd", "include"):
+            shutil.copytree(os.path.join(SRC, name), os.path.join(dst, name), ignore=skip)
+        for name in ("pytest.ini", "bench.py", "__graft_entry__.py"):
+            shutil.copy2(os.path.join(SRC, name), dst)
         target = os.path.join(dst, "oracle", "rra_oracle.py")
         for name, a, b in MUTANTS:
             if only and not any(o in name for o in only):
